@@ -1,0 +1,699 @@
+// Host side of the C ABI declared in include/gqa.h: cache state, argument
+// checks, the page allocator and the kernel launches.
+//
+// Sources: page "Prefill：整层状态演化与 KV 建立" (2.1 preconditions fail before
+// anything runs; 2.5 LayerCache and invariants; 2.6 write the valid tokens'
+// used K/V at their positions, then attend; 2.11 position ids restarting after
+// reuse are a failure) and page "KV Cache 与 Prefill/Decode 推理路径"
+// (PagedAttention lesson: per-request block table, logical block t/16 at offset
+// t%16, any free block when the last one is full; prompt-edit lesson: keep
+// [0,m), truncate, re-prefill the suffix).
+//
+// Rules fixed by this library where the pages leave a choice:
+//  * slot = position: the valid tokens of a call must carry positions
+//    c, c+1, ... where c is the current length of that (sequence, layer);
+//  * the valid tokens of a row form one contiguous run;
+//  * a page serves every layer of its sequence; the first layer that needs a
+//    logical page takes it from the front of the free list, in batch order then
+//    logical-page order; truncation returns pages to the back in ascending
+//    logical order, remap returns source pages in the order given;
+//  * every check runs before any state changes or any launch.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "gqa.h"
+#include "common.hpp"
+
+#define GQA_EXPORT extern "C" __attribute__((visibility("default")))
+
+using gqa::kPage;
+using gqa::kMaxSeqPerLaunch;
+
+struct gqa_cache {
+  gqa_cache_config cfg;
+  void* k_pool;
+  void* v_pool;
+  int32_t* d_table;
+  float* d_rope;
+  std::deque<int32_t> free_list;
+  std::vector<std::vector<int32_t>> pages;  // per sequence: physical page of each logical page
+  std::vector<int32_t> len;                 // [seq * num_layers + layer]
+  std::vector<float> rope_host;             // [max_position][d/2][2]
+  bool rope_uploaded = false;
+  std::vector<std::pair<int32_t, int32_t>> pending;  // block-table entries to write on the device
+  int elt = 2;
+  int64_t layer_elems = 0;                  // elements of one layer of a pool
+  int64_t page_elems = 0;                   // elements of one page (all kv heads) of one layer
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+gqa_status fail(gqa_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kDecodeTargetBlocks = 2048;   // workgroups a decode launch aims for
+constexpr int kDecodeMinPages = 4;          // pages per split at least (one per wave)
+
+gqa_status check_config(const gqa_cache_config* c) {
+  if (!c) return fail(GQA_ERR_ARG, "config is null");
+  if (c->num_layers < 1 || c->num_kv_heads < 1 || c->num_pages < 1 || c->max_seqs < 1 ||
+      c->max_pages_per_seq < 1)
+    return fail(GQA_ERR_ARG, "layers, kv heads, pages, sequences and table width must be >= 1");
+  if (c->page_size != kPage) return fail(GQA_ERR_UNSUPPORTED, "page_size must be 16");
+  if (c->dtype != GQA_F32 && c->dtype != GQA_BF16) return fail(GQA_ERR_DTYPE, "unknown dtype");
+  if (c->head_dim < 1 || c->head_dim > 128) return fail(GQA_ERR_UNSUPPORTED, "head_dim must be 1..128");
+  if (c->dtype == GQA_BF16 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(GQA_ERR_UNSUPPORTED, "bf16 caches need head_dim 64 or 128");
+  if (c->rope_style != 0 && c->rope_style != 1) return fail(GQA_ERR_UNSUPPORTED, "rope_style must be 0 or 1");
+  if (c->rope_style == 1) {
+    if (c->head_dim % 2) return fail(GQA_ERR_ARG, "rotation needs an even head_dim");
+    if (c->max_position < 1) return fail(GQA_ERR_ARG, "max_position must be >= 1");
+    if (!(c->rope_theta > 0.0)) return fail(GQA_ERR_ARG, "rope_theta must be > 0");
+  }
+  return GQA_OK;
+}
+
+// Strided 4-D tensor of the cache dtype with the given logical shape.
+gqa_status check_tensor(const gqa_tensor* t, const char* name, int dtype, int64_t s0, int64_t s1, int64_t s2,
+                        int64_t s3) {
+  if (!t) return fail(GQA_ERR_ARG, std::string(name) + " is null");
+  if (t->dtype != dtype) return fail(GQA_ERR_DTYPE, std::string(name) + " dtype differs from the cache dtype");
+  const int64_t want[4] = {s0, s1, s2, s3};
+  for (int i = 0; i < 4; ++i)
+    if (t->shape[i] != want[i]) return fail(GQA_ERR_SHAPE, std::string(name) + " has the wrong shape");
+  if (t->stride[3] != 1) return fail(GQA_ERR_SHAPE, std::string(name) + " innermost stride must be 1");
+  for (int i = 0; i < 3; ++i)
+    if (t->stride[i] < 0) return fail(GQA_ERR_SHAPE, std::string(name) + " has a negative stride");
+  const int64_t numel = s0 * s1 * s2 * s3;
+  if (numel == 0) return GQA_OK;
+  if (!t->data) return fail(GQA_ERR_ARG, std::string(name) + " data is null");
+  const uintptr_t p = reinterpret_cast<uintptr_t>(t->data);
+  if (dtype == GQA_BF16) {
+    if (p % 16) return fail(GQA_ERR_SHAPE, std::string(name) + " must be 16-byte aligned");
+    for (int i = 0; i < 3; ++i)
+      if (t->stride[i] % 8) return fail(GQA_ERR_SHAPE, std::string(name) + " strides must keep rows 16-byte aligned");
+  } else if (p % 4) {
+    return fail(GQA_ERR_SHAPE, std::string(name) + " must be 4-byte aligned");
+  }
+  return GQA_OK;
+}
+
+gqa_status check_seqs(const gqa_cache* c, int32_t B, const int32_t* seq_ids) {
+  if (B < 0) return fail(GQA_ERR_ARG, "B must be >= 0");
+  if (B > 0 && !seq_ids) return fail(GQA_ERR_ARG, "seq_ids is null");
+  std::vector<char> seen(c->cfg.max_seqs, 0);
+  for (int b = 0; b < B; ++b) {
+    const int s = seq_ids[b];
+    if (s < 0 || s >= c->cfg.max_seqs) return fail(GQA_ERR_ARG, "sequence id out of range");
+    if (seen[s]) return fail(GQA_ERR_ARG, "a sequence appears twice in one call");
+    seen[s] = 1;
+  }
+  return GQA_OK;
+}
+
+struct AppendPlan {
+  int64_t n = 0;
+  std::vector<int32_t> row0, count, start, need;
+};
+
+// Every check of an append (mask, positions, capacity, page budget).
+gqa_status plan_append(const gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* K,
+                       const gqa_tensor* V, const uint8_t* mask, const int32_t* positions, AppendPlan* plan) {
+  const gqa_cache_config& cf = c->cfg;
+  if (!K || !V) return fail(GQA_ERR_ARG, "K or V is null");
+  const int64_t n = K->shape[2];
+  if (n < 0) return fail(GQA_ERR_SHAPE, "negative token count");
+  gqa_status st = check_tensor(K, "K", cf.dtype, B, cf.num_kv_heads, n, cf.head_dim);
+  if (st != GQA_OK) return st;
+  st = check_tensor(V, "V", cf.dtype, B, cf.num_kv_heads, n, cf.head_dim);
+  if (st != GQA_OK) return st;
+  if (B > 0 && n > 0 && (!mask || !positions)) return fail(GQA_ERR_ARG, "mask or positions is null");
+  plan->n = n;
+  plan->row0.assign(B, 0);
+  plan->count.assign(B, 0);
+  plan->start.assign(B, 0);
+  plan->need.assign(B, 0);
+  for (int b = 0; b < B; ++b) {
+    const uint8_t* m = mask + static_cast<int64_t>(b) * n;
+    int64_t first = -1, last = -1, cnt = 0;
+    for (int64_t i = 0; i < n; ++i) {
+      if (m[i] > 1) return fail(GQA_ERR_MASK, "mask entries must be 0 or 1");
+      if (m[i]) {
+        if (first < 0) first = i;
+        last = i;
+        ++cnt;
+      }
+    }
+    if (cnt && last - first + 1 != cnt) return fail(GQA_ERR_MASK, "valid tokens of a row must be contiguous");
+    plan->row0[b] = cnt ? static_cast<int32_t>(first) : 0;
+    plan->count[b] = static_cast<int32_t>(cnt);
+  }
+  for (int b = 0; b < B; ++b) {
+    const int s = seq_ids[b];
+    const int32_t c0 = c->len[static_cast<int64_t>(s) * cf.num_layers + layer];
+    plan->start[b] = c0;
+    const int32_t* p = positions + static_cast<int64_t>(b) * n + plan->row0[b];
+    for (int i = 0; i < plan->count[b]; ++i)
+      if (p[i] != c0 + i) return fail(GQA_ERR_POSITION, "positions must continue the cache: c_b, c_b+1, ...");
+    const int64_t end = static_cast<int64_t>(c0) + plan->count[b];
+    if (cf.rope_style == 1 && end > cf.max_position) return fail(GQA_ERR_POSITION, "position beyond max_position");
+    if (ceil_div(end, kPage) > cf.max_pages_per_seq)
+      return fail(GQA_ERR_OUT_OF_PAGES, "sequence exceeds its block-table capacity");
+  }
+  int64_t total_need = 0;
+  for (int b = 0; b < B; ++b) {
+    const int s = seq_ids[b];
+    const int64_t end = static_cast<int64_t>(plan->start[b]) + plan->count[b];
+    const int64_t have = static_cast<int64_t>(c->pages[s].size());
+    plan->need[b] = static_cast<int32_t>(std::max<int64_t>(0, ceil_div(end, kPage) - have));
+    total_need += plan->need[b];
+  }
+  if (total_need > static_cast<int64_t>(c->free_list.size())) return fail(GQA_ERR_OUT_OF_PAGES, "not enough free pages");
+  return GQA_OK;
+}
+
+void commit_append(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const AppendPlan& plan) {
+  const gqa_cache_config& cf = c->cfg;
+  for (int b = 0; b < B; ++b) {
+    const int s = seq_ids[b];
+    for (int k = 0; k < plan.need[b]; ++k) {
+      const int32_t page = c->free_list.front();
+      c->free_list.pop_front();
+      const int32_t lp = static_cast<int32_t>(c->pages[s].size());
+      c->pages[s].push_back(page);
+      c->pending.emplace_back(s * cf.max_pages_per_seq + lp, page);
+    }
+  }
+  for (int b = 0; b < B; ++b)
+    c->len[static_cast<int64_t>(seq_ids[b]) * cf.num_layers + layer] = plan.start[b] + plan.count[b];
+}
+
+gqa_status hip_fail(hipError_t e, const char* what) {
+  return fail(GQA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Upload the rotation table once and write pending block-table entries.
+gqa_status sync_metadata(gqa_cache* c, hipStream_t s) {
+  if (c->cfg.rope_style == 1 && !c->rope_uploaded) {
+    hipError_t e = hipMemcpyAsync(c->d_rope, c->rope_host.data(), c->rope_host.size() * sizeof(float),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "rotation table upload");
+    c->rope_uploaded = true;
+  }
+  size_t i = 0;
+  while (i < c->pending.size()) {
+    gqa::PatchArgs pa;
+    pa.table = c->d_table;
+    pa.n = 0;
+    for (; i < c->pending.size() && pa.n < gqa::kMaxPatchPerLaunch; ++i, ++pa.n) {
+      pa.index[pa.n] = c->pending[i].first;
+      pa.value[pa.n] = c->pending[i].second;
+    }
+    hipError_t e = gqa::launch_table_patch(pa, s);
+    if (e != hipSuccess) return hip_fail(e, "block-table patch");
+  }
+  c->pending.clear();
+  return GQA_OK;
+}
+
+template <typename T>
+T* layer_base(void* pool, const gqa_cache* c, int layer) {
+  return static_cast<T*>(pool) + static_cast<int64_t>(layer) * c->layer_elems;
+}
+
+gqa_status launch_append_all(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* K,
+                             const gqa_tensor* V, const AppendPlan& plan, hipStream_t s) {
+  const gqa_cache_config& cf = c->cfg;
+  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+    gqa::AppendArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.K = static_cast<const char*>(K->data) + b0 * K->stride[0] * c->elt;
+    a.V = static_cast<const char*>(V->data) + b0 * V->stride[0] * c->elt;
+    a.k_s0 = K->stride[0]; a.k_s1 = K->stride[1]; a.k_s2 = K->stride[2];
+    a.v_s0 = V->stride[0]; a.v_s1 = V->stride[1]; a.v_s2 = V->stride[2];
+    a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.table = c->d_table;
+    a.table_w = cf.max_pages_per_seq;
+    a.Hkv = cf.num_kv_heads;
+    a.d = cf.head_dim;
+    a.nseq = nb;
+    a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    int grid_x = 0;
+    for (int j = 0; j < nb; ++j) {
+      const int b = b0 + j;
+      a.meta.seq[j] = seq_ids[b];
+      a.meta.start[j] = plan.start[b];
+      a.meta.count[j] = plan.count[b];
+      a.meta.row0[j] = plan.row0[b];
+      a.meta.total[j] = plan.start[b] + plan.count[b];
+      if (plan.count[b] > 0) {
+        const int first = plan.start[b] / kPage;
+        const int last = (plan.start[b] + plan.count[b] - 1) / kPage;
+        grid_x = std::max(grid_x, last - first + 1);
+      }
+    }
+    if (grid_x == 0) continue;
+    hipError_t e = gqa::launch_append(a, cf.dtype, grid_x, s);
+    if (e != hipSuccess) return hip_fail(e, "cache write launch");
+  }
+  return GQA_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ lifecycle
+
+GQA_EXPORT gqa_status gqa_cache_buffer_sizes(const gqa_cache_config* cfg, size_t* k_pool_bytes, size_t* v_pool_bytes,
+                                             size_t* page_table_bytes, size_t* rope_table_bytes) {
+  gqa_status st = check_config(cfg);
+  if (st != GQA_OK) return st;
+  const size_t elt = cfg->dtype == GQA_BF16 ? 2 : 4;
+  const size_t pool = static_cast<size_t>(cfg->num_layers) * cfg->num_pages * cfg->num_kv_heads * kPage *
+                      cfg->head_dim * elt;
+  if (k_pool_bytes) *k_pool_bytes = pool;
+  if (v_pool_bytes) *v_pool_bytes = pool;
+  if (page_table_bytes) *page_table_bytes = static_cast<size_t>(cfg->max_seqs) * cfg->max_pages_per_seq * 4;
+  if (rope_table_bytes)
+    *rope_table_bytes = cfg->rope_style == 1 ? static_cast<size_t>(cfg->max_position) * cfg->head_dim * 4 : 0;
+  return GQA_OK;
+}
+
+GQA_EXPORT gqa_status gqa_cache_create(const gqa_cache_config* cfg, void* k_pool, void* v_pool, int32_t* page_table,
+                                       void* rope_table, const int32_t* free_list_order, gqa_cache** out) {
+  gqa_status st = check_config(cfg);
+  if (st != GQA_OK) return st;
+  if (!out) return fail(GQA_ERR_ARG, "out is null");
+  if (!k_pool || !v_pool || !page_table) return fail(GQA_ERR_ARG, "pool or page-table pointer is null");
+  if (cfg->rope_style == 1 && !rope_table) return fail(GQA_ERR_ARG, "rope_table is null");
+  if (reinterpret_cast<uintptr_t>(k_pool) % 16 || reinterpret_cast<uintptr_t>(v_pool) % 16)
+    return fail(GQA_ERR_ARG, "pools must be 16-byte aligned");
+  std::vector<int32_t> order(cfg->num_pages);
+  if (free_list_order) {
+    std::vector<char> seen(cfg->num_pages, 0);
+    for (int i = 0; i < cfg->num_pages; ++i) {
+      const int32_t p = free_list_order[i];
+      if (p < 0 || p >= cfg->num_pages || seen[p]) return fail(GQA_ERR_ARG, "free_list_order is not a permutation");
+      seen[p] = 1;
+      order[i] = p;
+    }
+  } else {
+    for (int i = 0; i < cfg->num_pages; ++i) order[i] = i;
+  }
+  gqa_cache* c = new (std::nothrow) gqa_cache();
+  if (!c) return fail(GQA_ERR_ARG, "out of host memory");
+  c->cfg = *cfg;
+  c->k_pool = k_pool;
+  c->v_pool = v_pool;
+  c->d_table = page_table;
+  c->d_rope = static_cast<float*>(rope_table);
+  c->free_list.assign(order.begin(), order.end());
+  c->pages.assign(cfg->max_seqs, {});
+  c->len.assign(static_cast<size_t>(cfg->max_seqs) * cfg->num_layers, 0);
+  c->elt = cfg->dtype == GQA_BF16 ? 2 : 4;
+  c->page_elems = static_cast<int64_t>(cfg->num_kv_heads) * kPage * cfg->head_dim;
+  c->layer_elems = static_cast<int64_t>(cfg->num_pages) * c->page_elems;
+  if (cfg->rope_style == 1) {
+    // pair i turns by p * theta^(-2i/d): frequency and angle in double, cos and
+    // sin from the C library, rounded once to float32
+    const int half = cfg->head_dim / 2;
+    std::vector<double> inv(half);
+    for (int i = 0; i < half; ++i) inv[i] = std::pow(cfg->rope_theta, -2.0 * i / cfg->head_dim);
+    c->rope_host.resize(static_cast<size_t>(cfg->max_position) * cfg->head_dim);
+    for (int64_t p = 0; p < cfg->max_position; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = static_cast<double>(p) * inv[i];
+        c->rope_host[(p * half + i) * 2] = static_cast<float>(std::cos(ang));
+        c->rope_host[(p * half + i) * 2 + 1] = static_cast<float>(std::sin(ang));
+      }
+  }
+  *out = c;
+  return GQA_OK;
+}
+
+GQA_EXPORT gqa_status gqa_cache_destroy(gqa_cache* cache) {
+  delete cache;
+  return GQA_OK;
+}
+
+// ------------------------------------------------------------------ append / prefill
+
+GQA_EXPORT gqa_status kv_cache_append(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
+                                      const gqa_tensor* K, const gqa_tensor* V, const uint8_t* valid_mask,
+                                      const int32_t* positions, void* stream) {
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  if (layer < 0 || layer >= c->cfg.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
+  gqa_status st = check_seqs(c, B, seq_ids);
+  if (st != GQA_OK) return st;
+  AppendPlan plan;
+  st = plan_append(c, layer, B, seq_ids, K, V, valid_mask, positions, &plan);
+  if (st != GQA_OK) return st;
+  commit_append(c, layer, B, seq_ids, plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sync_metadata(c, s);
+  if (st != GQA_OK) return st;
+  return launch_append_all(c, layer, B, seq_ids, K, V, plan, s);
+}
+
+GQA_EXPORT gqa_status gqa_prefill(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
+                                  const gqa_tensor* Q, const gqa_tensor* K, const gqa_tensor* V,
+                                  const uint8_t* valid_mask, const int32_t* positions, const gqa_tensor* O,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const gqa_cache_config& cf = c->cfg;
+  if (layer < 0 || layer >= cf.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
+  gqa_status st = check_seqs(c, B, seq_ids);
+  if (st != GQA_OK) return st;
+  if (!Q || !O || !K) return fail(GQA_ERR_ARG, "Q, K or O is null");
+  const int64_t n = K->shape[2];
+  const int64_t Hq = Q->shape[1];
+  if (Hq < 1 || Hq % cf.num_kv_heads) return fail(GQA_ERR_SHAPE, "Hkv must divide Hq");
+  st = check_tensor(Q, "Q", cf.dtype, B, Hq, n, cf.head_dim);
+  if (st != GQA_OK) return st;
+  st = check_tensor(O, "O", cf.dtype, B, Hq, n, cf.head_dim);
+  if (st != GQA_OK) return st;
+  AppendPlan plan;
+  st = plan_append(c, layer, B, seq_ids, K, V, valid_mask, positions, &plan);
+  if (st != GQA_OK) return st;
+  commit_append(c, layer, B, seq_ids, plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sync_metadata(c, s);
+  if (st != GQA_OK) return st;
+  st = launch_append_all(c, layer, B, seq_ids, K, V, plan, s);
+  if (st != GQA_OK) return st;
+  if (n == 0) return GQA_OK;
+  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+    gqa::AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.Q = static_cast<const char*>(Q->data) + b0 * Q->stride[0] * c->elt;
+    a.q_s0 = Q->stride[0]; a.q_s1 = Q->stride[1]; a.q_s2 = Q->stride[2];
+    a.O = static_cast<char*>(O->data) + b0 * O->stride[0] * c->elt;
+    a.o_s0 = O->stride[0]; a.o_s1 = O->stride[1]; a.o_s2 = O->stride[2];
+    a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.table = c->d_table;
+    a.table_w = cf.max_pages_per_seq;
+    a.Hq = static_cast<int32_t>(Hq);
+    a.Hkv = cf.num_kv_heads;
+    a.d = cf.head_dim;
+    a.n_rect = static_cast<int32_t>(n);
+    a.nseq = nb;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
+    a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    for (int j = 0; j < nb; ++j) {
+      const int b = b0 + j;
+      a.meta.seq[j] = seq_ids[b];
+      a.meta.start[j] = plan.start[b];
+      a.meta.count[j] = plan.count[b];
+      a.meta.row0[j] = plan.row0[b];
+      a.meta.total[j] = plan.start[b] + plan.count[b];
+    }
+    hipError_t e = cf.dtype == GQA_BF16 ? gqa::launch_prefill_bf16(a, s) : gqa::launch_attend_f32(a, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  }
+  return GQA_OK;
+}
+
+// ------------------------------------------------------------------ decode
+
+GQA_EXPORT size_t gqa_workspace_size(const gqa_cache* c, int32_t B, int32_t Hq) {
+  if (!c || B < 0 || Hq < 1) return 0;
+  const int64_t splits = ceil_div(kDecodeTargetBlocks, c->cfg.num_kv_heads) + B;
+  const int64_t floats = splits * Hq * (static_cast<int64_t>(c->cfg.head_dim) + 2);
+  return static_cast<size_t>(floats * 4 + 512);
+}
+
+GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
+                                 const gqa_tensor* q, const int32_t* valid_lengths, const gqa_tensor* o,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const gqa_cache_config& cf = c->cfg;
+  if (layer < 0 || layer >= cf.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
+  gqa_status st = check_seqs(c, B, seq_ids);
+  if (st != GQA_OK) return st;
+  if (!q || !o) return fail(GQA_ERR_ARG, "q or o is null");
+  const int64_t Hq = q->shape[1];
+  if (Hq < 1 || Hq % cf.num_kv_heads) return fail(GQA_ERR_SHAPE, "Hkv must divide Hq");
+  st = check_tensor(q, "q", cf.dtype, B, Hq, 1, cf.head_dim);
+  if (st != GQA_OK) return st;
+  st = check_tensor(o, "o", cf.dtype, B, Hq, 1, cf.head_dim);
+  if (st != GQA_OK) return st;
+  if (B > 0 && !valid_lengths) return fail(GQA_ERR_ARG, "valid_lengths is null");
+  for (int b = 0; b < B; ++b) {
+    const int32_t have = c->len[static_cast<int64_t>(seq_ids[b]) * cf.num_layers + layer];
+    if (valid_lengths[b] != have) return fail(GQA_ERR_CACHE, "valid length differs from the cache length");
+    if (have < 1) return fail(GQA_ERR_CACHE, "decode needs at least one cached token");
+  }
+  if (B == 0) return GQA_OK;
+  const int G = static_cast<int>(Hq / cf.num_kv_heads);
+  const int hchunks = (G + 15) / 16;
+  int64_t total_pages = 0;
+  for (int b = 0; b < B; ++b) total_pages += ceil_div(valid_lengths[b], kPage);
+  const int64_t work = total_pages * cf.num_kv_heads * hchunks;
+  const int pps = static_cast<int>(std::max<int64_t>(kDecodeMinPages, ceil_div(work, kDecodeTargetBlocks)));
+  int64_t total_splits = 0;
+  for (int b = 0; b < B; ++b) total_splits += ceil_div(ceil_div(valid_lengths[b], kPage), pps);
+  const bool bf16 = cf.dtype == GQA_BF16;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (bf16 && total_splits > B) {
+    const size_t need = gqa_workspace_size(c, B, static_cast<int32_t>(Hq));
+    if (!workspace || ws_bytes < need) return fail(GQA_ERR_ARG, "workspace missing or smaller than gqa_workspace_size");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
+    const int64_t max_splits = ceil_div(kDecodeTargetBlocks, cf.num_kv_heads) + B;
+    part_o = static_cast<float*>(workspace);
+    part_ml = part_o + max_splits * Hq * cf.head_dim;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sync_metadata(c, s);
+  if (st != GQA_OK) return st;
+  int64_t split_base = 0;
+  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+    const void* lk = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    const void* lv = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    if (!bf16) {
+      gqa::AttnArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.Q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
+      a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1]; a.q_s2 = q->stride[2];
+      a.O = static_cast<char*>(o->data) + b0 * o->stride[0] * c->elt;
+      a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1]; a.o_s2 = o->stride[2];
+      a.k_pool = lk;
+      a.v_pool = lv;
+      a.table = c->d_table;
+      a.table_w = cf.max_pages_per_seq;
+      a.Hq = static_cast<int32_t>(Hq);
+      a.Hkv = cf.num_kv_heads;
+      a.d = cf.head_dim;
+      a.n_rect = 1;
+      a.nseq = nb;
+      a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
+      a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+      for (int j = 0; j < nb; ++j) {
+        a.meta.seq[j] = seq_ids[b0 + j];
+        a.meta.start[j] = valid_lengths[b0 + j] - 1;
+        a.meta.count[j] = 1;
+        a.meta.row0[j] = 0;
+        a.meta.total[j] = valid_lengths[b0 + j];
+      }
+      hipError_t e = gqa::launch_attend_f32(a, s);
+      if (e != hipSuccess) return hip_fail(e, "decode launch");
+      continue;
+    }
+    gqa::DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
+    a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1];
+    a.o = static_cast<char*>(o->data) + b0 * o->stride[0] * c->elt;
+    a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1];
+    a.k_pool = lk;
+    a.v_pool = lv;
+    a.table = c->d_table;
+    a.table_w = cf.max_pages_per_seq;
+    a.Hq = static_cast<int32_t>(Hq);
+    a.Hkv = cf.num_kv_heads;
+    a.d = cf.head_dim;
+    a.nseq = nb;
+    a.pages_per_split = pps;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
+    a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    a.part_o = part_o ? part_o + split_base * Hq * cf.head_dim : nullptr;
+    a.part_ml = part_ml ? part_ml + split_base * Hq * 2 : nullptr;
+    int32_t off = 0;
+    bool any_multi = false;
+    for (int j = 0; j < nb; ++j) {
+      const int T = valid_lengths[b0 + j];
+      a.meta.seq[j] = seq_ids[b0 + j];
+      a.meta.start[j] = T - 1;
+      a.meta.count[j] = 1;
+      a.meta.row0[j] = 0;
+      a.meta.total[j] = T;
+      a.split_off[j] = off;
+      const int ns = static_cast<int>(ceil_div(ceil_div(T, kPage), pps));
+      any_multi |= ns > 1;
+      off += ns;
+    }
+    a.split_off[nb] = off;
+    hipError_t e = gqa::launch_decode_bf16(a, off, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (any_multi) {
+      gqa::MergeArgs m;
+      std::memset(&m, 0, sizeof(m));
+      m.o = a.o;
+      m.o_s0 = a.o_s0;
+      m.o_s1 = a.o_s1;
+      m.part_o = a.part_o;
+      m.part_ml = a.part_ml;
+      m.Hq = a.Hq;
+      m.d = a.d;
+      m.nseq = nb;
+      std::memcpy(m.split_off, a.split_off, sizeof(m.split_off));
+      e = gqa::launch_decode_merge(m, s);
+      if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+    }
+    split_base += off;
+  }
+  return GQA_OK;
+}
+
+// ------------------------------------------------------------------ truncate / remap
+
+GQA_EXPORT gqa_status kv_cache_truncate(gqa_cache* c, int32_t seq_id, int32_t m) {
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const gqa_cache_config& cf = c->cfg;
+  if (seq_id < 0 || seq_id >= cf.max_seqs) return fail(GQA_ERR_ARG, "sequence id out of range");
+  if (m < 0) return fail(GQA_ERR_ARG, "negative truncation point");
+  int32_t longest = 0;
+  for (int l = 0; l < cf.num_layers; ++l) {
+    int32_t& n = c->len[static_cast<int64_t>(seq_id) * cf.num_layers + l];
+    n = std::min(n, m);
+    longest = std::max(longest, n);
+  }
+  const size_t keep = static_cast<size_t>(ceil_div(longest, kPage));
+  std::vector<int32_t>& pl = c->pages[seq_id];
+  for (size_t i = keep; i < pl.size(); ++i) c->free_list.push_back(pl[i]);
+  if (pl.size() > keep) pl.resize(keep);
+  return GQA_OK;
+}
+
+GQA_EXPORT gqa_status kv_cache_remap(gqa_cache* c, int32_t n, const int32_t* src, const int32_t* dst, void* stream) {
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const gqa_cache_config& cf = c->cfg;
+  if (n < 0) return fail(GQA_ERR_ARG, "negative page count");
+  if (n == 0) return GQA_OK;
+  if (!src || !dst) return fail(GQA_ERR_ARG, "src or dst is null");
+  std::vector<int64_t> owner(cf.num_pages, -1);   // seq * max_pages_per_seq + logical page
+  for (int s = 0; s < cf.max_seqs; ++s)
+    for (size_t i = 0; i < c->pages[s].size(); ++i) owner[c->pages[s][i]] = static_cast<int64_t>(s) * cf.max_pages_per_seq + i;
+  std::vector<char> is_free(cf.num_pages, 0);
+  for (int32_t p : c->free_list) is_free[p] = 1;
+  std::vector<char> seen_src(cf.num_pages, 0), seen_dst(cf.num_pages, 0);
+  for (int i = 0; i < n; ++i) {
+    if (src[i] < 0 || src[i] >= cf.num_pages || dst[i] < 0 || dst[i] >= cf.num_pages)
+      return fail(GQA_ERR_ARG, "page id out of range");
+    if (seen_src[src[i]] || seen_dst[dst[i]]) return fail(GQA_ERR_ARG, "repeated page");
+    seen_src[src[i]] = seen_dst[dst[i]] = 1;
+  }
+  for (int i = 0; i < n; ++i) {
+    if (owner[src[i]] < 0) return fail(GQA_ERR_CACHE, "source page is not in use");
+    if (!is_free[dst[i]]) return fail(GQA_ERR_CACHE, "destination page is not free");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  gqa_status st = sync_metadata(c, s);
+  if (st != GQA_OK) return st;
+  for (int i0 = 0; i0 < n; i0 += gqa::kMaxPatchPerLaunch) {
+    gqa::CopyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k_pool = c->k_pool;
+    a.v_pool = c->v_pool;
+    a.layer_stride = c->layer_elems;
+    a.page_elems = c->page_elems;
+    a.elt_bytes = c->elt;
+    a.n = std::min(n - i0, gqa::kMaxPatchPerLaunch);
+    for (int j = 0; j < a.n; ++j) {
+      a.src[j] = src[i0 + j];
+      a.dst[j] = dst[i0 + j];
+    }
+    hipError_t e = gqa::launch_page_copy(a, cf.num_layers, s);
+    if (e != hipSuccess) return hip_fail(e, "page copy launch");
+  }
+  for (int i = 0; i < n; ++i) {
+    const int64_t ow = owner[src[i]];
+    const int sq = static_cast<int>(ow / cf.max_pages_per_seq);
+    const int lp = static_cast<int>(ow % cf.max_pages_per_seq);
+    c->pages[sq][lp] = dst[i];
+    c->pending.emplace_back(sq * cf.max_pages_per_seq + lp, dst[i]);
+    c->free_list.erase(std::find(c->free_list.begin(), c->free_list.end(), dst[i]));
+  }
+  for (int i = 0; i < n; ++i) c->free_list.push_back(src[i]);
+  return sync_metadata(c, s);
+}
+
+// ------------------------------------------------------------------ queries
+
+GQA_EXPORT gqa_status gqa_cache_length(const gqa_cache* c, int32_t seq_id, int32_t layer, int32_t* out) {
+  if (!c || !out) return fail(GQA_ERR_ARG, "null argument");
+  if (seq_id < 0 || seq_id >= c->cfg.max_seqs || layer < 0 || layer >= c->cfg.num_layers)
+    return fail(GQA_ERR_ARG, "sequence or layer out of range");
+  *out = c->len[static_cast<int64_t>(seq_id) * c->cfg.num_layers + layer];
+  return GQA_OK;
+}
+
+GQA_EXPORT gqa_status gqa_cache_page_table(const gqa_cache* c, int32_t seq_id, int32_t* out, int32_t cap,
+                                           int32_t* n_out) {
+  if (!c || !n_out) return fail(GQA_ERR_ARG, "null argument");
+  if (seq_id < 0 || seq_id >= c->cfg.max_seqs) return fail(GQA_ERR_ARG, "sequence id out of range");
+  const std::vector<int32_t>& pl = c->pages[seq_id];
+  *n_out = static_cast<int32_t>(pl.size());
+  if (static_cast<int64_t>(pl.size()) > cap) return fail(GQA_ERR_ARG, "output capacity too small");
+  if (!pl.empty() && !out) return fail(GQA_ERR_ARG, "out is null");
+  for (size_t i = 0; i < pl.size(); ++i) out[i] = pl[i];
+  return GQA_OK;
+}
+
+GQA_EXPORT gqa_status gqa_cache_free_pages(const gqa_cache* c, int32_t* out) {
+  if (!c || !out) return fail(GQA_ERR_ARG, "null argument");
+  *out = static_cast<int32_t>(c->free_list.size());
+  return GQA_OK;
+}
+
+GQA_EXPORT gqa_status gqa_cache_check(const gqa_cache* c) {
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const gqa_cache_config& cf = c->cfg;
+  std::vector<int> count(cf.num_pages, 0);
+  for (int s = 0; s < cf.max_seqs; ++s) {
+    int32_t lmin = INT32_MAX, lmax = 0;
+    for (int l = 0; l < cf.num_layers; ++l) {
+      const int32_t n = c->len[static_cast<int64_t>(s) * cf.num_layers + l];
+      lmin = std::min(lmin, n);
+      lmax = std::max(lmax, n);
+    }
+    if (lmin != lmax) return fail(GQA_ERR_CACHE, "sequence " + std::to_string(s) + ": layer lengths differ");
+    if (static_cast<int64_t>(c->pages[s].size()) != ceil_div(lmax, kPage))
+      return fail(GQA_ERR_CACHE, "sequence " + std::to_string(s) + ": page count does not match its length");
+    for (int32_t p : c->pages[s]) ++count[p];
+  }
+  for (int32_t p : c->free_list) ++count[p];
+  for (int p = 0; p < cf.num_pages; ++p)
+    if (count[p] != 1) return fail(GQA_ERR_CACHE, "page " + std::to_string(p) + " is lost or owned twice");
+  return GQA_OK;
+}
+
+GQA_EXPORT const char* gqa_last_error(void) { return g_err.c_str(); }

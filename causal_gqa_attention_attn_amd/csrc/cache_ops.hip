@@ -1,0 +1,123 @@
+// Cache-side kernels: block-table patches, the fused rotation + paged cache
+// write, and physical page copies.
+//
+// Cache contract (page "Prefill：整层状态演化与 KV 建立", section 2.5): the
+// cache holds the keys actually used by attention, i.e. after the position
+// rotation, plus the values, at slot = position.  Paging (page "KV Cache 与
+// Prefill/Decode 推理路径", PagedAttention lesson): slot t lives in logical page
+// t / 16 at offset t % 16; the block table maps logical to physical pages.
+//
+// Physical layout per layer:  K  [page][kv head][16 slots][d]
+//                             V  [page][kv head][d][16 slots]   (V^T per page)
+// so attention kernels read a K page row-major and a V page already transposed,
+// which is the operand order the matrix cores want for S = K q and O^T = V^T P^T.
+#include "common.hpp"
+#include "device.hpp"
+
+namespace gqa {
+
+__global__ __launch_bounds__(256) void table_patch_kernel(PatchArgs a) {
+  for (int i = threadIdx.x; i < a.n; i += blockDim.x) a.table[a.index[i]] = a.value[i];
+}
+
+hipError_t launch_table_patch(const PatchArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(table_patch_kernel, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+
+// grid: x = logical page within the call's slot range, y = kv head, z = sequence.
+// Each block writes the slots of one (page, head) that this call appends.
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int b = blockIdx.z;
+  const int g = blockIdx.y;
+  const int nb = a.meta.count[b];
+  if (nb == 0) return;
+  const int seq = a.meta.seq[b];
+  const int c0 = a.meta.start[b];
+  const int r0 = a.meta.row0[b];
+  const int lp = c0 / kPage + static_cast<int>(blockIdx.x);
+  const int slot_lo = max(c0, lp * kPage);
+  const int slot_hi = min(c0 + nb, lp * kPage + kPage);
+  if (slot_lo >= slot_hi) return;
+  const int nslots = slot_hi - slot_lo;
+  const int d = a.d;
+  const int half = d / 2;
+  const int64_t phys = a.table[static_cast<int64_t>(seq) * a.table_w + lp];
+  T* kp = static_cast<T*>(a.k_pool) + (phys * a.Hkv + g) * (kPage * d);
+  T* vp = static_cast<T*>(a.v_pool) + (phys * a.Hkv + g) * (d * kPage);
+  const T* kin = static_cast<const T*>(a.K) + b * a.k_s0 + g * a.k_s1;
+  const T* vin = static_cast<const T*>(a.V) + b * a.v_s0 + g * a.v_s1;
+
+  // keys: rotate in float32 (pairs i, i + d/2), round to the storage dtype
+  for (int e = threadIdx.x; e < nslots * d; e += blockDim.x) {
+    const int si = e / d;
+    const int dd = e - si * d;
+    const int slot = slot_lo + si;
+    const T* row = kin + static_cast<int64_t>(r0 + slot - c0) * a.k_s2;
+    T out;
+    if (a.rope) {
+      const bool lo = dd < half;
+      const int i = lo ? dd : dd - half;
+      const float c = a.rope[(static_cast<int64_t>(slot) * half + i) * 2];
+      const float s = a.rope[(static_cast<int64_t>(slot) * half + i) * 2 + 1];
+      const float own = to_f32<T>(row[dd]);
+      const float other = to_f32<T>(row[lo ? dd + half : dd - half]);
+      float xo, yo;
+      if (lo) {
+        rotate_pair(own, other, c, s, xo, yo);
+        out = from_f32<T>(xo);
+      } else {
+        rotate_pair(other, own, c, s, xo, yo);
+        out = from_f32<T>(yo);
+      }
+    } else {
+      out = row[dd];
+    }
+    kp[(slot % kPage) * d + dd] = out;
+  }
+  // values: bit copy into the d-major page
+  for (int e = threadIdx.x; e < nslots * d; e += blockDim.x) {
+    const int dd = e / nslots;
+    const int si = e - dd * nslots;
+    const int slot = slot_lo + si;
+    vp[dd * kPage + (slot % kPage)] = vin[static_cast<int64_t>(r0 + slot - c0) * a.v_s2 + dd];
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, int dtype, int grid_x, hipStream_t s) {
+  dim3 grid(grid_x, a.Hkv, a.nseq);
+  if (dtype == 0)
+    hipLaunchKernelGGL(append_kernel<float>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// grid: x = pair, y = layer, z = 0 for K, 1 for V.  Copies one page of all kv
+// heads in 16-byte units.
+__global__ __launch_bounds__(256) void page_copy_kernel(CopyArgs a) {
+  const int i = blockIdx.x;
+  const int64_t layer = blockIdx.y;
+  char* pool = static_cast<char*>(blockIdx.z == 0 ? a.k_pool : a.v_pool);
+  const int64_t page_bytes = a.page_elems * a.elt_bytes;
+  const int64_t layer_bytes = a.layer_stride * a.elt_bytes;
+  const u32x4* src = reinterpret_cast<const u32x4*>(pool + layer * layer_bytes + a.src[i] * page_bytes);
+  u32x4* dst = reinterpret_cast<u32x4*>(pool + layer * layer_bytes + a.dst[i] * page_bytes);
+  const int64_t n16 = page_bytes / 16;
+  for (int64_t e = threadIdx.x; e < n16; e += blockDim.x) dst[e] = src[e];
+}
+
+hipError_t launch_page_copy(const CopyArgs& a, int num_layers, hipStream_t s) {
+  hipLaunchKernelGGL(page_copy_kernel, dim3(a.n, num_layers, 2), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,113 @@
+// Kernel-argument structs shared by the host entry points and the kernels.
+// Every per-call piece of metadata travels in the kernel-argument segment, so a
+// launch never waits on a host-to-device copy.
+#pragma once
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+namespace gqa {
+
+constexpr int kPage = 16;          // tokens per page
+constexpr int kMaxSeqPerLaunch = 64;
+constexpr int kMaxPatchPerLaunch = 240;
+
+// Per-sequence metadata of one launch.
+//  start: position of the first valid token of the call (= cache length before
+//         an append, = T-1 for a decode query);
+//  count: valid tokens (queries) of the call;
+//  row0:  rectangular row of the first valid token;
+//  total: cache length the attention reads (keys at slots >= total are never
+//         valid, whatever the page holds).
+struct SeqMeta {
+  int32_t seq[kMaxSeqPerLaunch];
+  int32_t start[kMaxSeqPerLaunch];
+  int32_t count[kMaxSeqPerLaunch];
+  int32_t row0[kMaxSeqPerLaunch];
+  int32_t total[kMaxSeqPerLaunch];
+};
+
+struct PatchArgs {
+  int32_t* table;
+  int32_t n;
+  int32_t index[kMaxPatchPerLaunch];
+  int32_t value[kMaxPatchPerLaunch];
+};
+
+struct AppendArgs {
+  const void* K;
+  const void* V;
+  int64_t k_s0, k_s1, k_s2;   // element strides: batch, head, token
+  int64_t v_s0, v_s1, v_s2;
+  void* k_pool;               // this layer's pool base
+  void* v_pool;
+  const int32_t* table;
+  int32_t table_w;
+  int32_t Hkv, d, nseq;
+  const float* rope;          // [max_position][d/2][2] or nullptr
+  SeqMeta meta;
+};
+
+struct AttnArgs {
+  const void* Q;
+  int64_t q_s0, q_s1, q_s2;
+  void* O;
+  int64_t o_s0, o_s1, o_s2;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* table;
+  int32_t table_w;
+  int32_t Hq, Hkv, d, n_rect, nseq;
+  float scale;                // 1/sqrt(d)
+  float scale_log2;           // log2(e)/sqrt(d)
+  const float* rope;
+  SeqMeta meta;
+};
+
+struct DecodeArgs {
+  const void* q;
+  int64_t q_s0, q_s1;
+  void* o;
+  int64_t o_s0, o_s1;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* table;
+  int32_t table_w;
+  int32_t Hq, Hkv, d, nseq;
+  int32_t pages_per_split;
+  float scale_log2;
+  const float* rope;
+  float* part_o;              // [split][Hq][d]
+  float* part_ml;             // [split][Hq][2]  (running max in log2 units, sum)
+  int32_t split_off[kMaxSeqPerLaunch + 1];
+  SeqMeta meta;               // start = T-1, total = T
+};
+
+struct MergeArgs {
+  void* o;
+  int64_t o_s0, o_s1;
+  const float* part_o;
+  const float* part_ml;
+  int32_t Hq, d, nseq;
+  int32_t split_off[kMaxSeqPerLaunch + 1];
+};
+
+struct CopyArgs {
+  void* k_pool;               // whole pool (all layers)
+  void* v_pool;
+  int64_t layer_stride;       // elements per layer of a pool
+  int64_t page_elems;         // elements of one page (all kv heads)
+  int32_t n;
+  int32_t elt_bytes;
+  int32_t src[kMaxPatchPerLaunch];
+  int32_t dst[kMaxPatchPerLaunch];
+};
+
+hipError_t launch_table_patch(const PatchArgs& a, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int dtype, int grid_x, hipStream_t s);
+hipError_t launch_attend_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s);
+hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_page_copy(const CopyArgs& a, int num_layers, hipStream_t s);
+
+}  // namespace gqa

@@ -1,0 +1,195 @@
+/*
+ * gqa.h - masked causal grouped-query attention over a paged KV cache, on one
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: device pointers, host arrays,
+ * sizes and status codes; no C++ or framework types cross it.
+ *
+ * Sources (cited by page title and section):
+ *  [P1] "Prefill：整层状态演化与 KV 建立" (glenzli.com, vol. 2 ch. 2)
+ *       2.1 interface and preconditions, 2.2 mask M and the sentinel rule,
+ *       2.3 g(h), S, A, O, 2.5 LayerCache and cache invariants, 2.6 prefill
+ *       pseudocode (write the used K/V of the valid tokens, then attend),
+ *       2.11 failure table.
+ *  [P2] "模型执行：从 token 到 Prefill 与 Decode" (blog.mlxb.cc), sections on
+ *       prefill/decode shapes (decode: T-1 cached + 1 new = T keys).
+ *  [P3] "KV Cache 与 Prefill/Decode 推理路径" (wiki.maxwellmou.com, unit 10):
+ *       prompt-edit lesson (keep [0,m), truncate, incremental prefill),
+ *       PagedAttention lesson (block table, block floor(t/P), offset t mod P,
+ *       any free block, results unchanged), multi-turn incremental prefill
+ *       (old prefix fully visible, new block lower-triangular), RoPE paragraph
+ *       of the prefix-equality proof.
+ *
+ * Conventions common to every call
+ *  - Every function returns a gqa_status.  On any error nothing is launched
+ *    and no cache state changes ([P1] 2.1: fail before the first layer); the
+ *    message is available from gqa_last_error() on the calling thread.
+ *  - Calls that take `stream` (a hipStream_t, NULL = legacy default stream)
+ *    only enqueue work on it and return without synchronising.  All device
+ *    buffers must stay alive until that work has completed.
+ *  - A cache handle is not thread-safe.  Calls on one handle must be issued
+ *    from one thread and ordered on one stream.
+ *  - Host arrays (masks, positions, sequence ids, lengths) are read before the
+ *    call returns and may be reused immediately.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_ARG = -1,          /* null pointer, out-of-range id, repeated sequence   */
+  GQA_ERR_SHAPE = -2,        /* tensor shape/stride/alignment, Hkv does not divide Hq */
+  GQA_ERR_DTYPE = -3,        /* tensor dtype differs from the cache dtype          */
+  GQA_ERR_MASK = -4,         /* mask entry not 0/1, or valid tokens not contiguous */
+  GQA_ERR_POSITION = -5,     /* positions do not continue the cache ([P1] 2.11)    */
+  GQA_ERR_CACHE = -6,        /* cache state violated (lengths, pages in use)       */
+  GQA_ERR_OUT_OF_PAGES = -7, /* page pool or a sequence's block table is full      */
+  GQA_ERR_UNSUPPORTED = -8,  /* configuration outside what the kernels implement   */
+  GQA_ERR_HIP = -9           /* a HIP runtime call failed                          */
+} gqa_status;
+
+typedef enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+/* A strided 4-D device tensor.  stride[] is in elements; stride[3] must be 1.
+ * For bf16 the data pointer and stride[0..2] must keep every row 16-byte
+ * aligned.  Logical shapes used below:
+ *   Q, O   [B, Hq,  n, d]     K, V  [B, Hkv, n, d]     q, o (decode) [B, Hq, 1, d] */
+typedef struct gqa_tensor {
+  void* data;
+  int32_t dtype;     /* gqa_dtype */
+  int32_t reserved;
+  int64_t shape[4];
+  int64_t stride[4];
+} gqa_tensor;
+
+/* Cache configuration ([P1] 2.1 cache_config, 2.5 layout_metadata).
+ *  num_layers        layers; each has its own K/V and its own lengths.
+ *  num_kv_heads      Hkv.   head_dim: d, 64 or 128 for bf16, 1..128 for f32.
+ *  page_size         tokens per page; 16 is the only supported value.
+ *  num_pages         physical pages in the pool (a page serves all layers).
+ *  max_seqs          sequence ids are 0..max_seqs-1.
+ *  max_pages_per_seq block-table width.
+ *  dtype             storage dtype of the cache and of all Q/K/V/O tensors.
+ *  rope_style        0: no position transform; 1: rotation pairing dimension
+ *                    i with i + d/2 ([P3] RoPE paragraph; the pairing is this
+ *                    library's convention).  Keys are cached AFTER rotation
+ *                    ([P1] 2.5: the cache holds the keys used by attention).
+ *  max_position      rotation table rows: positions 0..max_position-1.
+ *  rope_theta        rotation base: pair i turns by p * theta^(-2i/d).      */
+typedef struct gqa_cache_config {
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t max_seqs;
+  int32_t max_pages_per_seq;
+  int32_t dtype;
+  int32_t rope_style;
+  int32_t max_position;
+  double rope_theta;
+} gqa_cache_config;
+
+typedef struct gqa_cache gqa_cache;
+
+/* Bytes of the four caller-owned device buffers for a configuration.
+ *  k_pool   [num_layers][num_pages][Hkv][page_size][d]   (key rows per page)
+ *  v_pool   [num_layers][num_pages][Hkv][d][page_size]   (values stored d-major
+ *           inside a page, so a page of one head is V^T; logical content is the
+ *           same as row-major V)
+ *  page_table int32 [max_seqs][max_pages_per_seq]
+ *  rope_table float32 pairs (cos, sin) [max_position][d/2]  (0 if rope_style 0) */
+gqa_status gqa_cache_buffer_sizes(const gqa_cache_config* cfg, size_t* k_pool_bytes,
+                                  size_t* v_pool_bytes, size_t* page_table_bytes,
+                                  size_t* rope_table_bytes);
+
+/* Create the host-side state of a cache over caller-owned device buffers.
+ * free_list_order: NULL for 0..num_pages-1, else a permutation of the pool that
+ * fixes the order in which free pages are handed out.  Page contents are not
+ * touched (fresh pages may hold anything; nothing beyond a sequence's length
+ * is ever used).  The rotation table is computed on the host here and copied to
+ * rope_table on the stream of the first call that launches work.
+ * No HIP call is made by this function. */
+gqa_status gqa_cache_create(const gqa_cache_config* cfg, void* k_pool, void* v_pool,
+                            int32_t* page_table, void* rope_table,
+                            const int32_t* free_list_order, gqa_cache** out);
+gqa_status gqa_cache_destroy(gqa_cache* cache);
+
+/* Append the valid tokens of K and V to layer `layer` of sequences seq_ids[0..B)
+ * ([P1] 2.6 cache.write_sequence; [P3] decode append, one K/V per token).
+ *  valid_mask  host uint8 [B][n], 1 = valid token; the valid tokens of each
+ *              row must form one contiguous run (padding on either side).
+ *  positions   host int32 [B][n]; for the valid tokens they must be
+ *              c_b, c_b+1, ... where c_b is the layer's current length for that
+ *              sequence (slot = position).  Padding entries are ignored.
+ * Keys are rotated (rope_style 1) in float32 and rounded to the cache dtype,
+ * values are copied bit-exactly.  Pages are taken from the free list when a
+ * layer first needs them: in batch order, then logical page order.
+ * B == 0 or n == 0 is a no-op. */
+gqa_status kv_cache_append(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
+                           const gqa_tensor* K, const gqa_tensor* V, const uint8_t* valid_mask,
+                           const int32_t* positions, void* stream);
+
+/* Prefill attention ([P1] 2.2-2.3, 2.6): kv_cache_append of K and V, then for
+ * every valid query token at position p and head h, with g = floor(h*Hkv/Hq),
+ *   O[b,h,i] = sum_{j<=p} softmax_j( <rot(q), k_used[g,j]> / sqrt(d) ) v[g,j]
+ * over the cache slots of the sequence.  With a non-empty cache this is the
+ * incremental (suffix) prefill of [P3]: the old prefix is fully visible.
+ * Rows of O for padding tokens are written as 0.  Q and O are [B,Hq,n,d] in the
+ * cache dtype; accumulation is float32.  workspace may be NULL (ws_bytes 0). */
+gqa_status gqa_prefill(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
+                       const gqa_tensor* Q, const gqa_tensor* K, const gqa_tensor* V,
+                       const uint8_t* valid_mask, const int32_t* positions, const gqa_tensor* O,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/* Decode attention ([P2] decode shapes; [P3] single-token decode needs no mask):
+ * one query per sequence at position T_b - 1 against all T_b cached slots of
+ * layer `layer`.  valid_lengths (host int32 [B]) must equal each sequence's
+ * current length in that layer (append the new token's K/V first) and be >= 1.
+ * q and o are [B,Hq,1,d].  workspace: device scratch for split partials, at
+ * least gqa_workspace_size(cache, B, Hq) bytes, 256-byte aligned. */
+gqa_status gqa_decode(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
+                      const gqa_tensor* q, const int32_t* valid_lengths, const gqa_tensor* o,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Prompt edit at position m ([P3] prompt-edit lesson): keep positions [0,m) in
+ * every layer of seq_id, drop the rest and return pages no layer still uses to
+ * the back of the free list (ascending logical order).  Host only; no launch.
+ * m beyond a layer's length leaves that layer unchanged.  m == 0 releases the
+ * sequence. */
+gqa_status kv_cache_truncate(gqa_cache* cache, int32_t seq_id, int32_t m);
+
+/* Move n physical pages ([P1] 2.2: the manager may move physical pages but not
+ * change which tokens they hold).  src_pages (host) must be in use, dst_pages
+ * (host) free and all distinct.  Copies every layer's K and V of each page on
+ * `stream`, rewrites the block tables and returns the source pages to the back
+ * of the free list in the order given. */
+gqa_status kv_cache_remap(gqa_cache* cache, int32_t n, const int32_t* src_pages,
+                          const int32_t* dst_pages, void* stream);
+
+/* Host-side queries. */
+gqa_status gqa_cache_length(const gqa_cache* cache, int32_t seq_id, int32_t layer, int32_t* out);
+gqa_status gqa_cache_page_table(const gqa_cache* cache, int32_t seq_id, int32_t* out, int32_t cap,
+                                int32_t* n_out);
+gqa_status gqa_cache_free_pages(const gqa_cache* cache, int32_t* out);
+/* Cache invariants ([P1] 2.5, invariants 2.2): every layer of a sequence has the
+ * same length, a sequence owns exactly ceil(length/page_size) pages, and every
+ * page is either free or owned by exactly one sequence.  GQA_ERR_CACHE if not. */
+gqa_status gqa_cache_check(const gqa_cache* cache);
+
+/* Device workspace bytes that suffice for gqa_decode with up to B sequences and
+ * Hq query heads, whatever their lengths.  gqa_prefill needs none. */
+size_t gqa_workspace_size(const gqa_cache* cache, int32_t B, int32_t Hq);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQA_H */

@@ -18,6 +18,7 @@ Reading fixed for this library (the pages leave it open):
 
 theta == 0 means "no position transform" (the toy decoder of page 2).
 """
+import functools
 import math
 
 import numpy as np
@@ -27,17 +28,24 @@ def inv_freq(theta: float, d: int) -> list:
     return [math.pow(theta, -2.0 * i / d) for i in range(d // 2)]
 
 
+@functools.lru_cache(maxsize=None)
+def _row(theta: float, d: int, p: int) -> tuple:
+    """(cos, sin) of every pair at position p, each rounded once to float32."""
+    c, s = [], []
+    for fi in inv_freq(theta, d):
+        a = float(p) * fi
+        c.append(math.cos(a))
+        s.append(math.sin(a))
+    return np.array(c, dtype=np.float32), np.array(s, dtype=np.float32)
+
+
 def cos_sin(theta: float, d: int, positions) -> tuple:
     """float32 cos and sin tables, shape [len(positions), d/2]."""
-    f = inv_freq(theta, d)
     pos = [int(p) for p in positions]
     c = np.empty((len(pos), d // 2), dtype=np.float32)
     s = np.empty((len(pos), d // 2), dtype=np.float32)
     for r, p in enumerate(pos):
-        for i, fi in enumerate(f):
-            a = float(p) * fi
-            c[r, i] = np.float32(math.cos(a))
-            s[r, i] = np.float32(math.sin(a))
+        c[r], s[r] = _row(float(theta), int(d), p)
     return c, s
 
 

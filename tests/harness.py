@@ -1,0 +1,125 @@
+"""Drive the HIP library and the oracle side by side on the same inputs.
+
+Inputs come from ``workloads`` (seeded); the library runs through the C ABI
+(``causal_gqa_attention_attn_amd``), the oracle through ``oracle.cache_model``.
+Comparisons: cache contents and block tables bit for bit; outputs to 1e-5
+absolute (float32) or 2e-2 of the row's largest magnitude (bfloat16, float32
+accumulation), per query row.
+"""
+import numpy as np
+import torch
+
+from oracle.cache_model import CacheModel
+
+F32_ATOL = 1e-5
+BF16_ROW_RTOL = 2e-2
+
+
+def as_f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float32).numpy()
+
+
+def dtype_tag(dt):
+    return "bf16" if dt == torch.bfloat16 else "f32"
+
+
+class Pair:
+    """One library cache and one oracle cache with the same configuration."""
+
+    def __init__(self, num_layers, Hkv, d, num_pages, max_seqs, max_pages_per_seq, dtype,
+                 theta, max_position=None, free_order=None):
+        import causal_gqa_attention_attn_amd as lib
+        self.lib = lib
+        self.dtype = dtype
+        mp = max_position if max_position else max_pages_per_seq * 16
+        self.gpu = lib.PagedCache(num_layers, Hkv, d, num_pages, max_seqs, max_pages_per_seq,
+                                  dtype=dtype, rope_theta=theta, max_position=mp,
+                                  free_list_order=free_order)
+        self.ref = CacheModel(num_layers, Hkv, d, 16, num_pages, max_seqs, max_pages_per_seq,
+                              dtype=dtype_tag(dtype), rope_theta=theta, max_position=mp,
+                              free_order=free_order)
+        self.ws = None
+
+    def workspace(self, B, Hq):
+        n = self.lib.gqa_workspace_size(self.gpu.handle, B, Hq)
+        if self.ws is None or self.ws.numel() < n:
+            self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        return self.ws
+
+    # ------------------------------------------------------------ calls
+    def prefill(self, layer, seq_ids, Q, K, V, mask, pos, oracle=True):
+        dev = [t.to("cuda") for t in (Q, K, V)]
+        O = torch.full_like(dev[0], float("nan"))
+        self.lib.gqa_prefill(self.gpu.handle, layer, seq_ids, dev[0], dev[1], dev[2], mask, pos, O)
+        torch.cuda.synchronize()
+        ref = None
+        if oracle:
+            ref = self.ref.prefill(layer, seq_ids, as_f32(Q), as_f32(K), as_f32(V),
+                                   mask.numpy(), pos.numpy())
+        else:
+            self.ref.append(layer, seq_ids, as_f32(K), as_f32(V), mask.numpy(), pos.numpy())
+        return O, ref
+
+    def append(self, layer, seq_ids, K, V, mask, pos):
+        self.lib.kv_cache_append(self.gpu.handle, layer, seq_ids, K.to("cuda"), V.to("cuda"), mask, pos)
+        self.ref.append(layer, seq_ids, as_f32(K), as_f32(V), mask.numpy(), pos.numpy())
+
+    def decode(self, layer, seq_ids, q, lengths, oracle=True):
+        qd = q.to("cuda")
+        o = torch.full_like(qd, float("nan"))
+        self.lib.gqa_decode(self.gpu.handle, layer, seq_ids, qd, lengths, o,
+                            self.workspace(len(seq_ids), q.shape[1]))
+        torch.cuda.synchronize()
+        ref = self.ref.decode(layer, seq_ids, as_f32(q), lengths) if oracle else None
+        return o, ref
+
+    def step(self, layer, seq_ids, st):
+        """One decode step: append the new token's k, v, then attend with q."""
+        B = len(seq_ids)
+        lens = [self.ref.cache_length(s, layer) for s in seq_ids]
+        mask = torch.ones((B, 1), dtype=torch.uint8)
+        pos = torch.tensor([[n] for n in lens], dtype=torch.int32)
+        self.append(layer, seq_ids, st.k, st.v, mask, pos)
+        return self.decode(layer, seq_ids, st.q, [n + 1 for n in lens])
+
+    def truncate(self, seq, m):
+        self.lib.kv_cache_truncate(self.gpu.handle, seq, m)
+        self.ref.truncate(seq, m)
+
+    # ------------------------------------------------------------ checks
+    def check_cache(self, seqs, layers=None):
+        torch.cuda.synchronize()
+        for s in seqs:
+            host_table = self.lib.gqa_cache_page_table(self.gpu.handle, s)
+            assert host_table == self.ref.page_table(s), f"block table of sequence {s}"
+            assert self.gpu.device_table(s, len(host_table)) == host_table, f"device table of sequence {s}"
+            for l in (layers if layers is not None else range(self.ref.L)):
+                assert self.lib.gqa_cache_length(self.gpu.handle, s, l) == self.ref.cache_length(s, l)
+                k, v = self.gpu.gather(s, l)
+                rk, rv = self.ref.keys(s, l), self.ref.values(s, l)
+                assert k.shape == rk.shape, (k.shape, rk.shape)
+                kk = k.to(torch.float32).numpy()
+                vv = v.to(torch.float32).numpy()
+                assert np.array_equal(kk.view(np.uint32), rk.view(np.uint32)), f"K cache seq {s} layer {l}"
+                assert np.array_equal(vv.view(np.uint32), rv.view(np.uint32)), f"V cache seq {s} layer {l}"
+
+
+def compare_rows(o_gpu: torch.Tensor, o_ref: np.ndarray, dtype, rows_mask=None):
+    """Per query row: float32 |o-ref| <= 1e-5; bf16 max|o-ref| <= 2e-2 * max|ref|.
+
+    Returns (max_abs_error, max_row_relative_error)."""
+    o = as_f32(o_gpu).astype(np.float64)
+    ref = np.asarray(o_ref, dtype=np.float64)
+    assert o.shape == ref.shape
+    if rows_mask is not None:
+        o = o[rows_mask]
+        ref = ref[rows_mask]
+    assert not np.isnan(o).any(), "NaN in a compared output row"
+    err = np.abs(o - ref)
+    scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+    rel = np.max(err, axis=-1) / np.maximum(np.squeeze(scale, -1), 1e-30)
+    if dtype == torch.float32:
+        assert err.max(initial=0) <= F32_ATOL, f"max abs error {err.max()}"
+    else:
+        assert rel.max(initial=0) <= BF16_ROW_RTOL, f"max row-relative error {rel.max()}"
+    return float(err.max(initial=0)), float(rel.max(initial=0))

@@ -1,0 +1,148 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/gqa.h declares, and rejects bad calls with the oracle's error class
+before any launch (no call here reaches the device)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "causal_gqa_attention_attn_amd", "libgqa.so")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gqa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:gqa_status|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_declared_symbols():
+    assert os.path.exists(LIB), "libgqa.so is not built"
+    lib = ctypes.CDLL(LIB)
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    import causal_gqa_attention_attn_amd as b
+    assert sorted(b.EXPORTS) == names
+
+
+FAKE = 1 << 20   # an aligned address that is never dereferenced: every call below fails validation
+
+
+class FakeTensor:
+    """Describes a device tensor by address, shape and strides only."""
+
+    def __init__(self, shape, dtype=torch.bfloat16):
+        self.shape = shape
+        self.dtype = dtype
+        st = [1] * 4
+        for i in (2, 1, 0):
+            st[i] = st[i + 1] * shape[i + 1]
+        self._stride = st
+
+    def dim(self):
+        return 4
+
+    def data_ptr(self):
+        return FAKE
+
+    def stride(self, i):
+        return self._stride[i]
+
+
+def _cache(lib, **kw):
+    cfg = dict(num_layers=2, num_kv_heads=2, head_dim=64, page_size=16, num_pages=4, max_seqs=2,
+               max_pages_per_seq=2, dtype=lib.BF16, rope_style=1, max_position=32, rope_theta=1e4)
+    cfg.update(kw)
+    c = lib._cfg(**cfg)
+    h = ctypes.c_void_p()
+    st = lib._lib.gqa_cache_create(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(h))
+    return st, h
+
+
+def test_config_checks():
+    import causal_gqa_attention_attn_amd as lib
+    st, _ = _cache(lib, page_size=8)
+    assert lib.STATUS[st] == "UNSUPPORTED"
+    st, _ = _cache(lib, head_dim=96)
+    assert lib.STATUS[st] == "UNSUPPORTED"
+    st, _ = _cache(lib, dtype=7)
+    assert lib.STATUS[st] == "DTYPE"
+    st, h = _cache(lib)
+    assert st == 0
+    lib.gqa_cache_check(h)
+    assert lib.gqa_cache_free_pages(h) == 4
+    assert lib.gqa_cache_length(h, 1, 1) == 0
+    lib.kv_cache_truncate(h, 0, 0)
+    with pytest.raises(lib.GqaError) as e:
+        lib.kv_cache_truncate(h, 5, 0)
+    assert e.value.name == "ARG"
+    lib.gqa_cache_destroy(h)
+
+
+def _bad_calls(lib, h):
+    """(name, callable) pairs that must fail validation."""
+    K = FakeTensor((1, 2, 3, 64))
+    ones = np.ones((1, 3), np.uint8)
+    pos = np.array([[0, 1, 2]], np.int32)
+    return {
+        "POSITION": lambda: lib.kv_cache_append(h, 0, [0], K, K, ones, pos + 1),
+        "MASK": lambda: lib.kv_cache_append(h, 0, [0], K, K, np.array([[1, 0, 1]], np.uint8), pos),
+        "SHAPE": lambda: lib.kv_cache_append(h, 0, [0], FakeTensor((1, 3, 3, 64)), K, ones, pos),
+        "DTYPE": lambda: lib.kv_cache_append(h, 0, [0], FakeTensor((1, 2, 3, 64), torch.float32), K, ones, pos),
+        "ARG": lambda: lib.kv_cache_append(h, 2, [0], K, K, ones, pos),
+        "OUT_OF_PAGES": lambda: lib.kv_cache_append(h, 0, [0], FakeTensor((1, 2, 40, 64)), FakeTensor((1, 2, 40, 64)),
+                                                    np.ones((1, 40), np.uint8), np.arange(40, dtype=np.int32)[None]),
+        "SHAPE_GQA": lambda: lib.gqa_prefill(h, 0, [0], FakeTensor((1, 3, 3, 64)), K, K, ones, pos,
+                                             FakeTensor((1, 3, 3, 64))),
+        "CACHE": lambda: lib.gqa_decode(h, 0, [0], FakeTensor((1, 4, 1, 64)), [1], FakeTensor((1, 4, 1, 64))),
+        "ARG_DUP": lambda: lib.kv_cache_append(h, 0, [0, 0], FakeTensor((2, 2, 3, 64)), FakeTensor((2, 2, 3, 64)),
+                                               np.ones((2, 3), np.uint8), np.array([[0, 1, 2]] * 2, np.int32)),
+    }
+
+
+def _oracle_codes():
+    from oracle.cache_model import CacheModel, OracleError
+    out = {}
+    z = lambda *s: np.zeros(s, np.float32)
+    ones = np.ones((1, 3), np.uint8)
+    pos = np.array([[0, 1, 2]])
+
+    def run(name, fn):
+        m = CacheModel(2, 2, 64, 16, 4, 2, 2, dtype="bf16", rope_theta=1e4, max_position=32)
+        try:
+            fn(m)
+        except OracleError as e:
+            out[name] = e.code
+
+    run("POSITION", lambda m: m.append(0, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), ones, pos + 1))
+    run("MASK", lambda m: m.append(0, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), np.array([[1, 0, 1]]), pos))
+    run("SHAPE", lambda m: m.append(0, [0], z(1, 3, 3, 64), z(1, 2, 3, 64), ones, pos))
+    run("DTYPE", lambda m: m.append(0, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), ones, pos, dtype="f32"))
+    run("ARG", lambda m: m.append(2, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), ones, pos))
+    run("OUT_OF_PAGES", lambda m: m.append(0, [0], z(1, 2, 40, 64), z(1, 2, 40, 64), np.ones((1, 40)),
+                                           np.arange(40)[None]))
+    run("SHAPE_GQA", lambda m: m.prefill(0, [0], z(1, 3, 3, 64), z(1, 2, 3, 64), z(1, 2, 3, 64), ones, pos))
+    run("CACHE", lambda m: m.decode(0, [0], z(1, 4, 1, 64), [1]))
+    run("ARG_DUP", lambda m: m.append(0, [0, 0], z(2, 2, 3, 64), z(2, 2, 3, 64), np.ones((2, 3)),
+                                      np.array([[0, 1, 2]] * 2)))
+    return out
+
+
+def test_rejections_match_oracle_without_gpu():
+    import causal_gqa_attention_attn_amd as lib
+    st, h = _cache(lib)
+    assert st == 0
+    expect = _oracle_codes()
+    for name, call in _bad_calls(lib, h).items():
+        with pytest.raises(lib.GqaError) as e:
+            call()
+        assert e.value.name == expect[name], (name, e.value.name, expect[name])
+    # nothing changed
+    lib.gqa_cache_check(h)
+    assert lib.gqa_cache_free_pages(h) == 4 and lib.gqa_cache_length(h, 0, 0) == 0
+    lib.gqa_cache_destroy(h)

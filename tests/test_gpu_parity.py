@@ -1,0 +1,362 @@
+"""GPU parity: the HIP library through its C ABI against the float64 oracle.
+
+Cache contents and block tables are compared bit for bit, outputs within
+1e-5 absolute (float32) or 2e-2 of the row maximum (bfloat16).  Small shapes
+span several tiles and ragged tails; full-size shapes (the Llama-3-8B- and
+Grok-1-shaped prefills, the 64-sequence serving decode) are checked on sampled
+rows that the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from harness import Pair, as_f32, compare_rows
+from test_oracle_pins import read_golden
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_gqa_attention_attn_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+# ------------------------------------------------------------------ tiny / worked example
+
+def test_worked_example_fp32():
+    say("case: worked 2-D example, fp32, Hq=1/2, Hkv=1")
+    g = read_golden("worked_2d.txt")
+    for Hq in (1, 2):
+        pair = Pair(1, 1, 2, 4, 1, 2, torch.float32, 0.0)
+        Q = torch.tensor([[1.0, 0.0], [1.0, 0.0]]).expand(1, Hq, 2, 2).contiguous()
+        K = torch.tensor([[[[1.0, 0.0], [0.0, 1.0]]]])
+        V = torch.tensor([[[[10.0, 0.0], [0.0, 20.0]]]])
+        mask = torch.ones((1, 2), dtype=torch.uint8)
+        pos = torch.tensor([[0, 1]], dtype=torch.int32)
+        O, ref = pair.prefill(0, [0], Q, K, V, mask, pos)
+        o = as_f32(O)
+        for h in range(Hq):
+            assert o[0, h, 0, 0] == 10.0 and o[0, h, 0, 1] == 0.0
+            o1, o2, tol = g["output_both"]
+            assert abs(o[0, h, 1, 0] - o1) <= tol and abs(o[0, h, 1, 1] - o2) <= tol
+        compare_rows(O, ref, torch.float32)
+        pair.check_cache([0])
+
+
+def test_tiny_fp32_prefill_and_decode():
+    say("case: tiny fp32 B=1 n=4 Hq=2 Hkv=1 d=4, 3 decode steps")
+    pre, steps = W.tiny()
+    pair = Pair(1, 1, 4, 4, 1, 4, torch.float32, 0.0)
+    O, ref = pair.prefill(0, [0], pre.Q, pre.K, pre.V, pre.mask, pre.positions)
+    compare_rows(O, ref, torch.float32)
+    pair.check_cache([0])
+    for st in steps:
+        o, r = pair.step(0, [0], st)
+        compare_rows(o, r, torch.float32)
+    pair.check_cache([0])
+
+
+def test_fp32_rotated_ragged():
+    say("case: fp32 with rotation, ragged, Hq=6 Hkv=2 d=32")
+    shape = W.AttnShape(B=3, n=37, Hq=6, Hkv=2, d=32, dtype=torch.float32, theta=1e4)
+    inp = W.prefill_inputs(shape, 77, lengths=[37, 20, 1])
+    pair = Pair(1, 2, 32, 16, 3, 4, torch.float32, 1e4)
+    O, ref = pair.prefill(0, [0, 1, 2], inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+    compare_rows(O, ref, torch.float32)
+    pair.check_cache([0, 1, 2])
+    for t in range(3):
+        o, r = pair.step(0, [0, 1, 2], W.decode_step_inputs(shape, 77, t))
+        compare_rows(o, r, torch.float32)
+
+
+# ------------------------------------------------------------------ bf16 prefill + decode
+
+@pytest.mark.parametrize("poison", [False, True])
+def test_ragged_bf16(poison):
+    say(f"case: ragged bf16 B=4 n=128 Hq=8 Hkv=2 d=64 poison={poison}, 16 decode steps")
+    inp = W.ragged(poison_padding=poison)
+    pair = Pair(1, 2, 64, 64, 4, 16, torch.bfloat16, 1e4)
+    O, ref = pair.prefill(0, [0, 1, 2, 3], inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+    valid = inp.mask.numpy().astype(bool)[:, None, :].repeat(8, 1)
+    compare_rows(O, ref, torch.bfloat16, rows_mask=valid)
+    assert torch.all(O.float().cpu()[~torch.from_numpy(valid)] == 0), "padding rows must be exact zeros"
+    pair.check_cache([0, 1, 2, 3])
+    for t in range(16):
+        o, r = pair.step(0, [0, 1, 2, 3], W.decode_step_inputs(inp.shape, 1002, t))
+        compare_rows(o, r, torch.bfloat16)
+    pair.check_cache([0, 1, 2, 3])
+
+
+GQA_SHAPES = [
+    # Hq, Hkv, d, lengths, theta
+    (8, 2, 64, [130, 77, 1], 1e4),
+    (32, 8, 128, [200, 64, 33], 5e5),
+    (48, 8, 128, [150, 97], 1e4),
+    (8, 8, 128, [70, 5], 1e4),
+    (16, 1, 128, [100, 31], 1e4),      # 16 query heads per KV head: two head chunks in prefill
+    (12, 1, 64, [90, 129], 1e4),       # 12 per group: a chunk of 8 and one of 4
+    (4, 2, 128, [300], 0.0),           # no rotation
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,lengths,theta", GQA_SHAPES)
+def test_gqa_shapes_bf16(Hq, Hkv, d, lengths, theta):
+    say(f"case: bf16 Hq={Hq} Hkv={Hkv} d={d} lengths={lengths} theta={theta}")
+    B, n = len(lengths), max(lengths)
+    shape = W.AttnShape(B=B, n=n, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=theta)
+    inp = W.prefill_inputs(shape, 4242 + Hq + d, lengths=lengths)
+    order = W.page_order(64, 99)
+    pair = Pair(1, Hkv, d, 64, B, 24, torch.bfloat16, theta, free_order=order)
+    ids = list(range(B))
+    O, ref = pair.prefill(0, ids, inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+    valid = inp.mask.numpy().astype(bool)[:, None, :].repeat(Hq, 1)
+    compare_rows(O, ref, torch.bfloat16, rows_mask=valid)
+    pair.check_cache(ids)
+    for t in range(3):
+        o, r = pair.step(0, ids, W.decode_step_inputs(shape, 4242, t))
+        compare_rows(o, r, torch.bfloat16)
+    pair.check_cache(ids)
+
+
+def test_incremental_prefill_and_edit():
+    say("case: edit at m, truncate, re-prefill suffix; bf16 Hq=32 Hkv=8 d=128")
+    n = 300
+    ms = [1, 137, 299]
+    B = len(ms)
+    shape = W.AttnShape(B=B, n=n, Hq=32, Hkv=8, d=128, dtype=torch.bfloat16, theta=5e5)
+    inp = W.prefill_inputs(shape, 31)
+    pair = Pair(2, 8, 128, 128, B, 32, torch.bfloat16, 5e5, free_order=W.page_order(128, 5))
+    ids = list(range(B))
+    for layer in range(2):
+        O, ref = pair.prefill(layer, ids, inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+        compare_rows(O, ref, torch.bfloat16)
+    pair.check_cache(ids)
+    prefix = {}
+    for s, m in zip(ids, ms):
+        prefix[s] = [pair.gpu.gather(s, l) for l in range(2)]
+        pair.truncate(s, m)
+    lens = [n - m for m in ms]
+    suffix = W.prefill_inputs(W.AttnShape(B=B, n=max(lens), Hq=32, Hkv=8, d=128,
+                                          dtype=torch.bfloat16, theta=5e5), 2006,
+                              lengths=lens, start=ms)
+    for layer in range(2):
+        O, ref = pair.prefill(layer, ids, suffix.Q, suffix.K, suffix.V, suffix.mask, suffix.positions)
+        valid = suffix.mask.numpy().astype(bool)[:, None, :].repeat(32, 1)
+        compare_rows(O, ref, torch.bfloat16, rows_mask=valid)
+    pair.check_cache(ids)
+    for s, m in zip(ids, ms):
+        for l in range(2):
+            k, v = pair.gpu.gather(s, l)
+            k0, v0 = prefix[s][l]
+            assert torch.equal(k[:, :m].view(torch.int16), k0[:, :m].view(torch.int16)), "prefix K changed"
+            assert torch.equal(v[:, :m].view(torch.int16), v0[:, :m].view(torch.int16)), "prefix V changed"
+
+
+# ------------------------------------------------------------------ invariants
+
+def _prefill_outputs(order, remap=False):
+    shape = W.AttnShape(B=2, n=200, Hq=32, Hkv=8, d=128, dtype=torch.bfloat16, theta=5e5)
+    inp = W.prefill_inputs(shape, 555, lengths=[200, 123])
+    pair = Pair(1, 8, 128, 64, 2, 16, torch.bfloat16, 5e5, free_order=order)
+    O, _ = pair.prefill(0, [0, 1], inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
+    if remap:
+        src = pair.lib.gqa_cache_page_table(pair.gpu.handle, 0)[:3]
+        free_now = [p for p in range(64) if p not in set(pair.lib.gqa_cache_page_table(pair.gpu.handle, 0)
+                                                         + pair.lib.gqa_cache_page_table(pair.gpu.handle, 1))]
+        dst = free_now[-3:]
+        pair.lib.kv_cache_remap(pair.gpu.handle, src, dst)
+        pair.ref.remap(src, dst)
+        pair.lib.gqa_cache_check(pair.gpu.handle)
+        pair.check_cache([0, 1])
+    st = W.decode_step_inputs(shape, 555, 0)
+    o, _ = pair.step(0, [0, 1], st)
+    return O.cpu(), o.cpu(), pair
+
+
+def test_page_permutation_and_remap_invariance():
+    say("case: paging invariance (identity vs permuted pool vs remapped pages)")
+    O1, o1, _ = _prefill_outputs(None)
+    O2, o2, _ = _prefill_outputs(W.page_order(64, 3003))
+    O3, o3, _ = _prefill_outputs(W.page_order(64, 3003), remap=True)
+    for a, b in ((O1, O2), (o1, o2), (o1, o3)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_batch_composition_invariance():
+    say("case: a sequence's output does not depend on its batch mates")
+    shape = W.AttnShape(B=3, n=150, Hq=32, Hkv=8, d=128, dtype=torch.bfloat16, theta=5e5)
+    inp = W.prefill_inputs(shape, 808, lengths=[150, 40, 99], poison_padding=True)
+    pair = Pair(1, 8, 128, 64, 3, 16, torch.bfloat16, 5e5)
+    O, _ = pair.prefill(0, [0, 1, 2], inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
+    solo = Pair(1, 8, 128, 64, 3, 16, torch.bfloat16, 5e5)
+    O1, _ = solo.prefill(0, [1], inp.Q[1:2, :, :40], inp.K[1:2, :, :40], inp.V[1:2, :, :40],
+                         inp.mask[1:2, :40], inp.positions[1:2, :40], oracle=False)
+    assert torch.equal(O[1:2, :, :40].cpu().view(torch.int16), O1.cpu().view(torch.int16))
+
+
+def test_cached_decode_equals_full_recompute_gpu():
+    say("case: GPU incremental cache bytes == GPU fresh prefill cache bytes")
+    shape = W.AttnShape(B=1, n=40, Hq=8, Hkv=2, d=64, dtype=torch.bfloat16, theta=1e4)
+    inp = W.prefill_inputs(shape, 21)
+    a = Pair(1, 2, 64, 16, 1, 8, torch.bfloat16, 1e4)
+    a.prefill(0, [0], inp.Q[:, :, :30], inp.K[:, :, :30], inp.V[:, :, :30], inp.mask[:, :30],
+              inp.positions[:, :30], oracle=False)
+    for t in range(30, 40):
+        a.append(0, [0], inp.K[:, :, t:t + 1], inp.V[:, :, t:t + 1], torch.ones((1, 1), dtype=torch.uint8),
+                 torch.tensor([[t]], dtype=torch.int32))
+    b = Pair(1, 2, 64, 16, 1, 8, torch.bfloat16, 1e4)
+    b.prefill(0, [0], inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
+    ka, va = a.gpu.gather(0, 0)
+    kb, vb = b.gpu.gather(0, 0)
+    assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
+    assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
+    a.check_cache([0])
+
+
+# ------------------------------------------------------------------ error paths on the device build
+
+def test_errors_match_oracle_gpu():
+    say("case: rejected calls return the oracle's error class and change nothing")
+    import causal_gqa_attention_attn_amd as lib
+    from oracle.cache_model import OracleError
+    pair = Pair(1, 2, 64, 4, 2, 2, torch.bfloat16, 1e4, max_position=1000)
+    shape = W.AttnShape(B=1, n=20, Hq=4, Hkv=2, d=64, dtype=torch.bfloat16, theta=1e4)
+    inp = W.prefill_inputs(shape, 1)
+    pair.prefill(0, [0], inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+    cases = {
+        "restart": (inp.mask, inp.positions),
+        "hole": (torch.tensor([[1, 0] + [1] * 18], dtype=torch.uint8), inp.positions + 20),
+    }
+    for name, (mask, pos) in cases.items():
+        with pytest.raises(lib.GqaError) as e:
+            pair.lib.kv_cache_append(pair.gpu.handle, 0, [0], inp.K.cuda(), inp.V.cuda(), mask, pos)
+        with pytest.raises(OracleError) as r:
+            pair.ref.append(0, [0], as_f32(inp.K), as_f32(inp.V), mask.numpy(), pos.numpy())
+        assert e.value.name == r.value.code, name
+    # the pool of 4 pages is exhausted by a second sequence of 60 tokens
+    big = W.prefill_inputs(W.AttnShape(B=1, n=60, Hq=4, Hkv=2, d=64, dtype=torch.bfloat16, theta=1e4), 2)
+    with pytest.raises(lib.GqaError) as e:
+        pair.lib.kv_cache_append(pair.gpu.handle, 0, [1], big.K.cuda(), big.V.cuda(), big.mask, big.positions)
+    assert e.value.name == "OUT_OF_PAGES"
+    assert lib.gqa_cache_free_pages(pair.gpu.handle) == 2
+    pair.check_cache([0, 1])
+    lib.gqa_cache_check(pair.gpu.handle)
+
+
+# ------------------------------------------------------------------ full sizes, sampled rows
+
+def _sampled_prefill(shape, inp, order, rows, layers=1, seqs=None):
+    B = shape.B
+    pages_per_seq = -(-shape.n // 16) + 4
+    pair = Pair(layers, shape.Hkv, shape.d, B * pages_per_seq, B, pages_per_seq, shape.dtype,
+                shape.theta, free_order=order)
+    ids = list(range(B))
+    O, _ = pair.prefill(0, ids, inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
+    Oc = O.cpu()
+    worst = 0.0
+    for b in (seqs if seqs is not None else ids):
+        q_rows = as_f32(inp.Q[b, :, rows, :])
+        ref = pair.ref.prefill_rows(0, b, q_rows, rows)
+        _, rel = compare_rows(Oc[b, :, rows, :], ref, shape.dtype)
+        worst = max(worst, rel)
+    pair.check_cache(seqs if seqs is not None else ids)
+    return pair, worst
+
+
+def test_llama_full_size_sampled():
+    say("case: Llama-3-8B-shaped prefill B=8 n=2048 Hq=32 Hkv=8 d=128, permuted pages, sampled rows")
+    inp = W.llama()
+    B, n = 8, 2048
+    order = W.page_order(B * (n // 16 + 4), 3003)
+    rows = [0, 1, 31, 32, 63, 64, 1000, 2046, 2047]
+    pair, worst = _sampled_prefill(W.LLAMA, inp, order, rows, seqs=[0, 7])
+    say(f"  worst row-relative error {worst:.3e}")
+    for t in range(2):
+        st = W.decode_step_inputs(W.LLAMA, 1003, t)
+        lens = [pair.ref.cache_length(s, 0) for s in range(B)]
+        pair.append(0, list(range(B)), st.k, st.v, torch.ones((B, 1), dtype=torch.uint8),
+                    torch.tensor([[x] for x in lens], dtype=torch.int32))
+        o, r = pair.decode(0, list(range(B)), st.q, [x + 1 for x in lens])
+        compare_rows(o, r, torch.bfloat16)
+
+
+def test_grok_full_size_sampled():
+    say("case: Grok-1-shaped prefill B=1 n=8192 Hq=48 Hkv=8 d=128, sampled rows; decode at T=8192")
+    inp = W.grok()
+    rows = [0, 1, 63, 64, 127, 128, 4095, 8000, 8190, 8191]
+    pair, worst = _sampled_prefill(W.GROK, inp, None, rows, layers=2)
+    say(f"  worst row-relative error {worst:.3e}")
+    # second layer holds 8191 tokens, then one appended token and a decode at T=8192
+    K2 = W.normal((1, 8, 8191, 128), 7004)
+    V2 = W.normal((1, 8, 8191, 128), 7005)
+    m = torch.ones((1, 8191), dtype=torch.uint8)
+    pair.append(1, [0], K2, V2, m, torch.arange(8191, dtype=torch.int32)[None])
+    st = W.decode_step_inputs(W.GROK, 1004, 0)
+    pair.append(1, [0], st.k, st.v, torch.ones((1, 1), dtype=torch.uint8), torch.tensor([[8191]], dtype=torch.int32))
+    o, r = pair.decode(1, [0], st.q, [8192])
+    compare_rows(o, r, torch.bfloat16)
+
+
+def test_serving_decode_full_size_sampled():
+    say("case: serving decode, 64 sequences, lengths log-uniform [512, 32768], Hq=32 Hkv=8 d=128")
+    import causal_gqa_attention_attn_amd as lib
+    from oracle.cache_model import CacheModel
+    lens = W.serving_lengths()
+    B = len(lens)
+    pages = sum(-(-(x + 1) // 16) for x in lens) + 8
+    order = W.page_order(pages, 1005)
+    cache = lib.PagedCache(1, 8, 128, pages, B, 32768 // 16 + 2, dtype=torch.bfloat16, rope_theta=5e5,
+                           max_position=32770, free_list_order=order)
+    n_max = max(lens)
+    # fill in one batched append (batch order fixes the page assignment)
+    K = torch.zeros((B, 8, n_max, 128), dtype=torch.bfloat16, device="cuda")
+    V = torch.zeros_like(K)
+    for b, L in enumerate(lens):
+        K[b, :, :L] = W.normal_device((8, L, 128), 91000 + b)
+        V[b, :, :L] = W.normal_device((8, L, 128), 92000 + b)
+    mask = W.right_padded_mask(lens, n_max)
+    pos = W.positions_for(mask, [0] * B)
+    lib.kv_cache_append(cache.handle, 0, list(range(B)), K, V, mask, pos)
+    del K, V
+    st = W.decode_step_inputs(W.SERVING, 1005, 0)
+    lib.kv_cache_append(cache.handle, 0, list(range(B)), st.k.cuda(), st.v.cuda(),
+                        torch.ones((B, 1), dtype=torch.uint8), torch.tensor([[x] for x in lens], dtype=torch.int32))
+    o = torch.empty((B, 32, 1, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(lib.gqa_workspace_size(cache.handle, B, 32), dtype=torch.uint8, device="cuda")
+    lib.gqa_decode(cache.handle, 0, list(range(B)), st.q.cuda(), [x + 1 for x in lens], o, ws)
+    torch.cuda.synchronize()
+    # block tables: a values-free run of the oracle's allocator with the same lengths
+    alloc = CacheModel(1, 1, 2, 16, pages, B, 32768 // 16 + 2, dtype="f32", free_order=order)
+    z = np.zeros((B, 1, n_max, 2), np.float32)
+    alloc.append(0, list(range(B)), z, z, mask.numpy(), pos.numpy())
+    alloc.append(0, list(range(B)), np.zeros((B, 1, 1, 2), np.float32), np.zeros((B, 1, 1, 2), np.float32),
+                 np.ones((B, 1), np.uint8), np.array([[x] for x in lens]))
+    for b in range(B):
+        assert lib.gqa_cache_page_table(cache.handle, b) == alloc.page_table(b)
+    # outputs of sampled sequences: shortest, longest and two others
+    order_by_len = sorted(range(B), key=lambda b: lens[b])
+    for b in [order_by_len[0], order_by_len[-1], 5, 40]:
+        L = lens[b]
+        ref = CacheModel(1, 8, 128, 16, -(-(L + 1) // 16), 1, -(-(L + 1) // 16), dtype="bf16",
+                         rope_theta=5e5, max_position=32770)
+        kb = W.normal_device((8, L, 128), 91000 + b).cpu()
+        vb = W.normal_device((8, L, 128), 92000 + b).cpu()
+        k = torch.cat([kb, st.k[b]], dim=1)[None]
+        v = torch.cat([vb, st.v[b]], dim=1)[None]
+        ref.append(0, [0], as_f32(k), as_f32(v), np.ones((1, L + 1), np.uint8), np.arange(L + 1)[None])
+        r = ref.decode(0, [0], as_f32(st.q[b:b + 1]), [L + 1])
+        compare_rows(o[b:b + 1], r, torch.bfloat16)
+        gk, gv = cache.gather(b, 0)
+        assert np.array_equal(gk.float().numpy().view(np.uint32), ref.keys(0, 0).view(np.uint32))
+        assert np.array_equal(gv.float().numpy().view(np.uint32), ref.values(0, 0).view(np.uint32))
+    cache.close()

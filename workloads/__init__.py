@@ -215,3 +215,11 @@ def edit_points(B=16, n=4096, seed=1006):
     """Edit positions m_b ~ U{1..n-1}, 0-based: tokens [0, m_b) are kept."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return [int(x) for x in rng.integers(1, n, size=B)]
+
+
+def normal_device(shape, seed, dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
+    """N(0,1) drawn on the device by torch's seeded generator (for fills too
+    large to draw on the host quickly); stored in ``dtype``."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dtype)
