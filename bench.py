@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Throughput of the attention path on one MI355X, Grok-1-shaped workload.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * kv_cache_truncate of the prompt sequence to 0 (host; frees its pages);
+  * prefill of B=1, n=8192, Hq=48, Hkv=8, d=128 (bf16, rotation theta 1e4):
+    kv_cache_append (validation, page reservation, block-table patch, fused
+    rotation + paged cache write) then gqa_attention (the MFMA causal kernel);
+    together these are exactly gqa_prefill;
+  * decode at T=8192 over a 64-layer bf16 cache: per layer kv_cache_append of
+    the new token (position 8191) and gqa_decode of one query reading all 8192
+    slots (2^31 bytes of K/V over the 64 layers).  The 64-layer loop is captured
+    once as a HIP graph and replayed, so every step does the same work.
+
+Inputs are resident in HBM before the timed region.  ``value`` is the causal
+prefill throughput 2*B*Hq*n^2*d / (append + attention time, HIP events);
+``decode`` reports the decode KV-read rate over the 64 layers.  ``roofline``
+is the prefill attention kernel: algorithmic flops of one launch over its
+event-timed duration, against the bf16 dense MFMA peak; ``roofline_decode``
+is one layer of the decode graph (append, split and merge kernels) against
+HBM.  ``cpu_baseline`` times the float64 oracle on a bounded sample of the
+same prefill (query rows spread over the sequence) on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+B, N, HQ, HKV, D, THETA, LAYERS = 1, 8192, 48, 8, 128, 1e4, 64
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(kernel_key, source):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the kernel source that is built now; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_sha256") != _sha(source):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, budget_s):
+    """Float64 oracle on a bounded sample: blocks of 64 query rows spread over
+    the sequence (all 48 heads), until ``budget_s`` seconds of work; reported as
+    causal TFLOP/s over the rows done (4*d*(p+1) flops per row and head)."""
+    import numpy as np
+    from oracle.cache_model import CacheModel
+    K = inp.K.float().numpy()
+    V = inp.V.float().numpy()
+    Q = inp.Q.float().numpy()
+    m = CacheModel(1, HKV, D, 16, N // 16, 1, N // 16, dtype="bf16", rope_theta=THETA, max_position=N)
+    m.append(0, [0], K, V, np.ones((1, N), np.uint8), np.arange(N)[None])
+    blocks = list(range(N - 64, -1, -N // 16))      # 16 blocks, heaviest first
+    rows_done, flops, t_used = 0, 0.0, 0.0
+    for r0 in blocks:
+        rows = list(range(r0, r0 + 64))
+        t = time.perf_counter()
+        m.prefill_rows(0, 0, Q[0, :, r0:r0 + 64], rows)
+        t_used += time.perf_counter() - t
+        rows_done += 64
+        flops += sum(4.0 * D * (p + 1) for p in rows) * HQ
+        if t_used >= budget_s:
+            break
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{rows_done} query rows x {HQ} heads of the n=8192 prefill (blocks of 64 rows "
+                      f"spread over the sequence, heaviest first), float64 numpy, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (profiling aid)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import causal_gqa_attention_attn_amd as lib
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    inp = W.grok()
+    Q, K, V = inp.Q.to(dev), inp.K.to(dev), inp.V.to(dev)
+    O = torch.empty_like(Q)
+    mask = inp.mask.numpy()
+    pos = inp.positions.numpy()
+    pages = N // 16 + 16
+    pre = lib.PagedCache(1, HKV, D, pages, 1, pages, dtype=torch.bfloat16, rope_theta=THETA, max_position=N + 16)
+
+    dec = lib.PagedCache(LAYERS, HKV, D, N // 16 + 2, 1, N // 16 + 2, dtype=torch.bfloat16,
+                         rope_theta=THETA, max_position=N + 16)
+    ones = torch.ones((1, N - 1), dtype=torch.uint8)
+    pfill = torch.arange(N - 1, dtype=torch.int32)[None]
+    for l in range(LAYERS):
+        kf = W.normal_device((1, HKV, N - 1, D), 70000 + l)
+        vf = W.normal_device((1, HKV, N - 1, D), 80000 + l)
+        lib.kv_cache_append(dec.handle, l, [0], kf, vf, ones, pfill)
+    steps_in = [W.decode_step_inputs(W.GROK, 1004, l) for l in range(LAYERS)]
+    qd = [s.q.to(dev) for s in steps_in]
+    kd = [s.k.to(dev) for s in steps_in]
+    vd = [s.v.to(dev) for s in steps_in]
+    od = [torch.empty_like(x) for x in qd]
+    ws = torch.zeros(lib.gqa_workspace_size(dec.handle, 1, HQ), dtype=torch.uint8, device=dev)
+    one = torch.ones((1, 1), dtype=torch.uint8)
+    p_new = torch.tensor([[N - 1]], dtype=torch.int32)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def decode_layers():
+        for l in range(LAYERS):
+            lib.kv_cache_append(dec.handle, l, [0], kd[l], vd[l], one, p_new)
+            lib.gqa_decode(dec.handle, l, [0], qd[l], [N], od[l], ws)
+
+    # The 64-layer decode loop is launch-bound from Python (two library calls per
+    # layer), so it is captured once in a HIP graph and replayed: every replay
+    # runs the same kernels with the same arguments (append at position 8191,
+    # decode at T=8192) as the eager loop.
+    decode_layers()                                  # eager warmup (uploads tables)
+    lib.kv_cache_truncate(dec.handle, 0, N - 1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_layers()
+    lib.kv_cache_truncate(dec.handle, 0, N - 1)
+    torch.cuda.synchronize()
+
+    def step(ev):
+        lib.kv_cache_truncate(pre.handle, 0, 0)
+        ev[0].record(stream)
+        lib.kv_cache_append(pre.handle, 0, [0], K, V, mask, pos)
+        ev[1].record(stream)
+        lib.gqa_attention(pre.handle, 0, [0], Q, mask, pos, O)
+        ev[2].record(stream)
+        if args.prefill_only:
+            return
+        ev[3].record(stream)
+        graph.replay()
+        ev[4].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    print("bench: warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(mk())
+    events = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    print("bench: timed steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    mean = lambda xs: sum(xs) / len(xs)
+    append_ms = mean([e[0].elapsed_time(e[1]) for e in events])
+    attn_ms = mean([e[1].elapsed_time(e[2]) for e in events])
+    prefill_ms = append_ms + attn_ms
+    flops = 2.0 * B * HQ * N * N * D
+    value = flops / (prefill_ms * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    src_prefill = os.path.join(ROOT, "causal_gqa_attention_attn_amd", "csrc", "prefill_bf16.hip")
+    out = {
+        "metric": "causal prefill attention TFLOP/s (% MFMA peak) + decode KV-read GB/s (% HBM)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V)",
+        "config": {"workload": "Grok-1-shaped attention: causal prefill B=1 n=8192 Hq=48 Hkv=8 d=128 "
+                               "(one layer, rotation theta 1e4, paged cache of 16-token pages) + "
+                               "decode at T=8192 over a 64-layer bf16 cache (2 GiB)",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)",
+                   "prefill_ms": round(prefill_ms, 4), "cache_write_ms": round(append_ms, 4),
+                   "attention_ms": round(attn_ms, 4),
+                   "causal_flops": flops, "causal_flops_exact": 2.0 * HQ * D * N * (N + 1)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("prefill_bf16_kernel<128>", src_prefill),
+                     "kernel": "prefill_bf16_kernel<128>"},
+    }
+    if not args.prefill_only:
+        span_ms = mean([e[3].elapsed_time(e[4]) for e in events])
+        kv_bytes = 2.0 * LAYERS * HKV * N * D * 2
+        per_layer_ms = span_ms / LAYERS
+        achieved = kv_bytes / LAYERS / (per_layer_ms * 1e-3) / 1e9
+        out["decode"] = {"value": round(kv_bytes / (span_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                         "kv_bytes_per_step": kv_bytes, "ms_64_layers": round(span_ms, 4),
+                         "note": "64 x (append of the new token + decode at T=8192), replayed as one HIP graph"}
+        src_dec = os.path.join(ROOT, "causal_gqa_attention_attn_amd", "csrc", "decode_bf16.hip")
+        out["roofline_decode"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                                  "traffic": _traffic("decode_bf16_kernel<128>", src_dec),
+                                  "kernel": "one layer of the replayed decode graph: append + decode_bf16_kernel<128> "
+                                            "+ decode_merge_kernel<128>, 32 MiB of K/V",
+                                  "layer_us": round(per_layer_ms * 1e3, 2)}
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,7 @@ F32, BF16 = 0, 1
 STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "MASK", -5: "POSITION",
           -6: "CACHE", -7: "OUT_OF_PAGES", -8: "UNSUPPORTED", -9: "HIP"}
 EXPORTS = ["gqa_cache_buffer_sizes", "gqa_cache_create", "gqa_cache_destroy", "kv_cache_append",
-           "gqa_prefill", "gqa_decode", "kv_cache_truncate", "kv_cache_remap", "gqa_cache_length",
+           "gqa_prefill", "gqa_attention", "gqa_decode", "kv_cache_truncate", "kv_cache_remap", "gqa_cache_length",
            "gqa_cache_page_table", "gqa_cache_free_pages", "gqa_cache_check", "gqa_workspace_size",
            "gqa_last_error"]
 
@@ -70,6 +70,7 @@ _sig = {
     "kv_cache_append": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _TP, _P, _P, _P],
     "gqa_prefill": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _TP, _TP, _P, _P, _TP, _P,
                     ctypes.c_size_t, _P],
+    "gqa_attention": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _P, _P, _TP, _P, ctypes.c_size_t, _P],
     "gqa_decode": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _P, _TP, _P, ctypes.c_size_t, _P],
     "kv_cache_truncate": [_P, ctypes.c_int32, ctypes.c_int32],
     "kv_cache_remap": [_P, ctypes.c_int32, _P, _P, _P],
@@ -182,6 +183,16 @@ def gqa_prefill(handle, layer, seq_ids, Q, K, V, valid_mask, positions, O, works
     _check(_lib.gqa_prefill(handle, layer, len(ids), _ptr(ids), ctypes.byref(tq), ctypes.byref(tk),
                             ctypes.byref(tv), _ptr(m), _ptr(p), ctypes.byref(to), ws, nbytes,
                             _stream(stream)), "gqa_prefill")
+
+
+def gqa_attention(handle, layer, seq_ids, Q, valid_mask, positions, O, workspace=None, stream=None):
+    ids = _host_i32(seq_ids)
+    m, p = _host_u8(valid_mask), _host_i32(positions)
+    tq, to = _tensor(Q), _tensor(O)
+    ws = None if workspace is None else workspace.data_ptr()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.gqa_attention(handle, layer, len(ids), _ptr(ids), ctypes.byref(tq), _ptr(m), _ptr(p),
+                              ctypes.byref(to), ws, nbytes, _stream(stream)), "gqa_attention")
 
 
 def gqa_decode(handle, layer, seq_ids, q, valid_lengths, o, workspace=None, stream=None):

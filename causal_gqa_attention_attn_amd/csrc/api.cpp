@@ -62,8 +62,14 @@ gqa_status fail(gqa_status s, const std::string& msg) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kDecodeTargetBlocks = 2048;   // workgroups a decode launch aims for
-constexpr int kDecodeMinPages = 4;          // pages per split at least (one per wave)
+#ifndef GQA_DECODE_TARGET_BLOCKS
+#define GQA_DECODE_TARGET_BLOCKS 512
+#endif
+#ifndef GQA_DECODE_MIN_PAGES
+#define GQA_DECODE_MIN_PAGES 8
+#endif
+constexpr int kDecodeTargetBlocks = GQA_DECODE_TARGET_BLOCKS;   // workgroups a decode launch aims for
+constexpr int kDecodeMinPages = GQA_DECODE_MIN_PAGES;           // pages per split at least
 
 gqa_status check_config(const gqa_cache_config* c) {
   if (!c) return fail(GQA_ERR_ARG, "config is null");
@@ -122,6 +128,22 @@ gqa_status check_seqs(const gqa_cache* c, int32_t B, const int32_t* seq_ids) {
   return GQA_OK;
 }
 
+gqa_status valid_run(const uint8_t* m, int64_t n, int64_t* row0, int64_t* count) {
+  int64_t first = -1, last = -1, cnt = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (m[i] > 1) return fail(GQA_ERR_MASK, "mask entries must be 0 or 1");
+    if (m[i]) {
+      if (first < 0) first = i;
+      last = i;
+      ++cnt;
+    }
+  }
+  if (cnt && last - first + 1 != cnt) return fail(GQA_ERR_MASK, "valid tokens of a row must be contiguous");
+  *row0 = cnt ? first : 0;
+  *count = cnt;
+  return GQA_OK;
+}
+
 struct AppendPlan {
   int64_t n = 0;
   std::vector<int32_t> row0, count, start, need;
@@ -145,18 +167,10 @@ gqa_status plan_append(const gqa_cache* c, int32_t layer, int32_t B, const int32
   plan->start.assign(B, 0);
   plan->need.assign(B, 0);
   for (int b = 0; b < B; ++b) {
-    const uint8_t* m = mask + static_cast<int64_t>(b) * n;
-    int64_t first = -1, last = -1, cnt = 0;
-    for (int64_t i = 0; i < n; ++i) {
-      if (m[i] > 1) return fail(GQA_ERR_MASK, "mask entries must be 0 or 1");
-      if (m[i]) {
-        if (first < 0) first = i;
-        last = i;
-        ++cnt;
-      }
-    }
-    if (cnt && last - first + 1 != cnt) return fail(GQA_ERR_MASK, "valid tokens of a row must be contiguous");
-    plan->row0[b] = cnt ? static_cast<int32_t>(first) : 0;
+    int64_t run0 = 0, cnt = 0;
+    gqa_status sr = valid_run(mask + static_cast<int64_t>(b) * n, n, &run0, &cnt);
+    if (sr != GQA_OK) return sr;
+    plan->row0[b] = static_cast<int32_t>(run0);
     plan->count[b] = static_cast<int32_t>(cnt);
   }
   for (int b = 0; b < B; ++b) {
@@ -268,6 +282,49 @@ gqa_status launch_append_all(gqa_cache* c, int32_t layer, int32_t B, const int32
     if (grid_x == 0) continue;
     hipError_t e = gqa::launch_append(a, cf.dtype, grid_x, s);
     if (e != hipSuccess) return hip_fail(e, "cache write launch");
+  }
+  return GQA_OK;
+}
+
+
+// Causal attention of each row's valid queries (positions start[b].., count[b]
+// of them, from rectangular row row0[b]) against slots [0, position] of the
+// layer; total[b] = written length of the sequence in that layer.
+gqa_status launch_attention(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* Q,
+                            const gqa_tensor* O, int64_t n, const int32_t* start, const int32_t* count,
+                            const int32_t* row0, const int32_t* total, hipStream_t s) {
+  const gqa_cache_config& cf = c->cfg;
+  const int64_t Hq = Q->shape[1];
+  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+    gqa::AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.Q = static_cast<const char*>(Q->data) + b0 * Q->stride[0] * c->elt;
+    a.q_s0 = Q->stride[0]; a.q_s1 = Q->stride[1]; a.q_s2 = Q->stride[2];
+    a.O = static_cast<char*>(O->data) + b0 * O->stride[0] * c->elt;
+    a.o_s0 = O->stride[0]; a.o_s1 = O->stride[1]; a.o_s2 = O->stride[2];
+    a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.table = c->d_table;
+    a.table_w = cf.max_pages_per_seq;
+    a.Hq = static_cast<int32_t>(Hq);
+    a.Hkv = cf.num_kv_heads;
+    a.d = cf.head_dim;
+    a.n_rect = static_cast<int32_t>(n);
+    a.nseq = nb;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
+    a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    for (int j = 0; j < nb; ++j) {
+      const int b = b0 + j;
+      a.meta.seq[j] = seq_ids[b];
+      a.meta.start[j] = start[b];
+      a.meta.count[j] = count[b];
+      a.meta.row0[j] = row0[b];
+      a.meta.total[j] = total[b];
+    }
+    hipError_t e = cf.dtype == GQA_BF16 ? gqa::launch_prefill_bf16(a, s) : gqa::launch_attend_f32(a, s);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
   }
   return GQA_OK;
 }
@@ -396,47 +453,80 @@ GQA_EXPORT gqa_status gqa_prefill(gqa_cache* c, int32_t layer, int32_t B, const 
   st = launch_append_all(c, layer, B, seq_ids, K, V, plan, s);
   if (st != GQA_OK) return st;
   if (n == 0) return GQA_OK;
-  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
-    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
-    gqa::AttnArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.Q = static_cast<const char*>(Q->data) + b0 * Q->stride[0] * c->elt;
-    a.q_s0 = Q->stride[0]; a.q_s1 = Q->stride[1]; a.q_s2 = Q->stride[2];
-    a.O = static_cast<char*>(O->data) + b0 * O->stride[0] * c->elt;
-    a.o_s0 = O->stride[0]; a.o_s1 = O->stride[1]; a.o_s2 = O->stride[2];
-    a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
-    a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
-    a.table = c->d_table;
-    a.table_w = cf.max_pages_per_seq;
-    a.Hq = static_cast<int32_t>(Hq);
-    a.Hkv = cf.num_kv_heads;
-    a.d = cf.head_dim;
-    a.n_rect = static_cast<int32_t>(n);
-    a.nseq = nb;
-    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
-    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
-    a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
-    for (int j = 0; j < nb; ++j) {
-      const int b = b0 + j;
-      a.meta.seq[j] = seq_ids[b];
-      a.meta.start[j] = plan.start[b];
-      a.meta.count[j] = plan.count[b];
-      a.meta.row0[j] = plan.row0[b];
-      a.meta.total[j] = plan.start[b] + plan.count[b];
-    }
-    hipError_t e = cf.dtype == GQA_BF16 ? gqa::launch_prefill_bf16(a, s) : gqa::launch_attend_f32(a, s);
-    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  std::vector<int32_t> totals(B);
+  for (int b = 0; b < B; ++b) totals[b] = plan.start[b] + plan.count[b];
+  return launch_attention(c, layer, B, seq_ids, Q, O, n, plan.start.data(), plan.count.data(), plan.row0.data(),
+                          totals.data(), s);
+}
+
+GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
+                                    const gqa_tensor* Q, const uint8_t* valid_mask, const int32_t* positions,
+                                    const gqa_tensor* O, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const gqa_cache_config& cf = c->cfg;
+  if (layer < 0 || layer >= cf.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
+  gqa_status st = check_seqs(c, B, seq_ids);
+  if (st != GQA_OK) return st;
+  if (!Q || !O) return fail(GQA_ERR_ARG, "Q or O is null");
+  const int64_t n = Q->shape[2];
+  const int64_t Hq = Q->shape[1];
+  if (n < 0) return fail(GQA_ERR_SHAPE, "negative token count");
+  if (Hq < 1 || Hq % cf.num_kv_heads) return fail(GQA_ERR_SHAPE, "Hkv must divide Hq");
+  st = check_tensor(Q, "Q", cf.dtype, B, Hq, n, cf.head_dim);
+  if (st != GQA_OK) return st;
+  st = check_tensor(O, "O", cf.dtype, B, Hq, n, cf.head_dim);
+  if (st != GQA_OK) return st;
+  if (B > 0 && n > 0 && (!valid_mask || !positions)) return fail(GQA_ERR_ARG, "mask or positions is null");
+  std::vector<int32_t> row0(B), count(B), start(B), totals(B);
+  for (int b = 0; b < B; ++b) {
+    int64_t run0 = 0, cnt = 0;
+    st = valid_run(valid_mask + static_cast<int64_t>(b) * n, n, &run0, &cnt);
+    if (st != GQA_OK) return st;
+    row0[b] = static_cast<int32_t>(run0);
+    count[b] = static_cast<int32_t>(cnt);
   }
-  return GQA_OK;
+  for (int b = 0; b < B; ++b) {
+    const int32_t have = c->len[static_cast<int64_t>(seq_ids[b]) * cf.num_layers + layer];
+    const int32_t* p = positions + static_cast<int64_t>(b) * n + row0[b];
+    start[b] = count[b] ? p[0] : 0;
+    for (int i = 0; i < count[b]; ++i)
+      if (p[i] != start[b] + i) return fail(GQA_ERR_POSITION, "query positions must be consecutive");
+    if (count[b] && (start[b] < 0 || static_cast<int64_t>(start[b]) + count[b] > have))
+      return fail(GQA_ERR_POSITION, "query positions must lie inside the cached length");
+    totals[b] = have;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sync_metadata(c, s);
+  if (st != GQA_OK) return st;
+  if (n == 0) return GQA_OK;
+  return launch_attention(c, layer, B, seq_ids, Q, O, n, start.data(), count.data(), row0.data(), totals.data(), s);
 }
 
 // ------------------------------------------------------------------ decode
 
+struct WsLayout {
+  int64_t max_splits, part_floats;
+  size_t bytes;
+};
+
+// Workspace: split partials, [split][kv head][head chunk of <= 16][d + 4]
+// float32 records (o, then m and l).  Whatever the lengths, a call makes at
+// most ceil(target / (Hkv * chunks)) + B splits per (kv head, chunk).
+WsLayout ws_layout(const gqa_cache* c, int64_t B, int64_t Hq) {
+  WsLayout w;
+  const int64_t chunks = ceil_div(std::max<int64_t>(1, Hq / c->cfg.num_kv_heads), 16);
+  const int64_t ys = c->cfg.num_kv_heads * chunks;
+  w.max_splits = ceil_div(kDecodeTargetBlocks, ys) + B;
+  w.part_floats = w.max_splits * ys * 16 * (static_cast<int64_t>(c->cfg.head_dim) + 4);
+  w.bytes = static_cast<size_t>(w.part_floats * 4);
+  return w;
+}
+
 GQA_EXPORT size_t gqa_workspace_size(const gqa_cache* c, int32_t B, int32_t Hq) {
   if (!c || B < 0 || Hq < 1) return 0;
-  const int64_t splits = ceil_div(kDecodeTargetBlocks, c->cfg.num_kv_heads) + B;
-  const int64_t floats = splits * Hq * (static_cast<int64_t>(c->cfg.head_dim) + 2);
-  return static_cast<size_t>(floats * 4 + 512);
+  return ws_layout(c, B, Hq).bytes;
 }
 
 GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
@@ -466,19 +556,21 @@ GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const i
   int64_t total_pages = 0;
   for (int b = 0; b < B; ++b) total_pages += ceil_div(valid_lengths[b], kPage);
   const int64_t work = total_pages * cf.num_kv_heads * hchunks;
-  const int pps = static_cast<int>(std::max<int64_t>(kDecodeMinPages, ceil_div(work, kDecodeTargetBlocks)));
+  int64_t max_pages = 0;
+  for (int b = 0; b < B; ++b) max_pages = std::max<int64_t>(max_pages, ceil_div(valid_lengths[b], kPage));
+  // at most 128 splits per sequence (the merge kernel holds one weight per split in LDS)
+  const int pps = static_cast<int>(std::max<int64_t>(std::max<int64_t>(kDecodeMinPages, ceil_div(work, kDecodeTargetBlocks)),
+                                                     ceil_div(max_pages, 128)));
   int64_t total_splits = 0;
   for (int b = 0; b < B; ++b) total_splits += ceil_div(ceil_div(valid_lengths[b], kPage), pps);
   const bool bf16 = cf.dtype == GQA_BF16;
   float* part_o = nullptr;
-  float* part_ml = nullptr;
   if (bf16 && total_splits > B) {
-    const size_t need = gqa_workspace_size(c, B, static_cast<int32_t>(Hq));
-    if (!workspace || ws_bytes < need) return fail(GQA_ERR_ARG, "workspace missing or smaller than gqa_workspace_size");
+    const WsLayout wl = ws_layout(c, B, Hq);
+    if (!workspace || ws_bytes < wl.bytes)
+      return fail(GQA_ERR_ARG, "workspace missing or smaller than gqa_workspace_size");
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
-    const int64_t max_splits = ceil_div(kDecodeTargetBlocks, cf.num_kv_heads) + B;
     part_o = static_cast<float*>(workspace);
-    part_ml = part_o + max_splits * Hq * cf.head_dim;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = sync_metadata(c, s);
@@ -534,10 +626,8 @@ GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const i
     a.pages_per_split = pps;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
-    a.part_o = part_o ? part_o + split_base * Hq * cf.head_dim : nullptr;
-    a.part_ml = part_ml ? part_ml + split_base * Hq * 2 : nullptr;
+    a.part_o = part_o ? part_o + split_base * cf.num_kv_heads * hchunks * 16 * (cf.head_dim + 4) : nullptr;
     int32_t off = 0;
-    bool any_multi = false;
     for (int j = 0; j < nb; ++j) {
       const int T = valid_lengths[b0 + j];
       a.meta.seq[j] = seq_ids[b0 + j];
@@ -546,28 +636,11 @@ GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const i
       a.meta.row0[j] = 0;
       a.meta.total[j] = T;
       a.split_off[j] = off;
-      const int ns = static_cast<int>(ceil_div(ceil_div(T, kPage), pps));
-      any_multi |= ns > 1;
-      off += ns;
+      off += static_cast<int>(ceil_div(ceil_div(T, kPage), pps));
     }
     a.split_off[nb] = off;
-    hipError_t e = gqa::launch_decode_bf16(a, off, s);
+    hipError_t e = gqa::launch_decode_bf16(a, off, off > nb, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
-    if (any_multi) {
-      gqa::MergeArgs m;
-      std::memset(&m, 0, sizeof(m));
-      m.o = a.o;
-      m.o_s0 = a.o_s0;
-      m.o_s1 = a.o_s1;
-      m.part_o = a.part_o;
-      m.part_ml = a.part_ml;
-      m.Hq = a.Hq;
-      m.d = a.d;
-      m.nseq = nb;
-      std::memcpy(m.split_off, a.split_off, sizeof(m.split_off));
-      e = gqa::launch_decode_merge(m, s);
-      if (e != hipSuccess) return hip_fail(e, "decode merge launch");
-    }
     split_base += off;
   }
   return GQA_OK;

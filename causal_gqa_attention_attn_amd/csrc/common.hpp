@@ -76,20 +76,11 @@ struct DecodeArgs {
   int32_t pages_per_split;
   float scale_log2;
   const float* rope;
-  float* part_o;              // [split][Hq][d]
-  float* part_ml;             // [split][Hq][2]  (running max in log2 units, sum)
+  float* part_o;              // split partials: [split][y][16][d + 4] (o, m, l)
   int32_t split_off[kMaxSeqPerLaunch + 1];
   SeqMeta meta;               // start = T-1, total = T
 };
 
-struct MergeArgs {
-  void* o;
-  int64_t o_s0, o_s1;
-  const float* part_o;
-  const float* part_ml;
-  int32_t Hq, d, nseq;
-  int32_t split_off[kMaxSeqPerLaunch + 1];
-};
 
 struct CopyArgs {
   void* k_pool;               // whole pool (all layers)
@@ -106,8 +97,7 @@ hipError_t launch_table_patch(const PatchArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int grid_x, hipStream_t s);
 hipError_t launch_attend_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s);
-hipError_t launch_decode_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, bool merge, hipStream_t s);
 hipError_t launch_page_copy(const CopyArgs& a, int num_layers, hipStream_t s);
 
 }  // namespace gqa

@@ -19,9 +19,11 @@
  *       of the prefix-equality proof.
  *
  * Conventions common to every call
- *  - Every function returns a gqa_status.  On any error nothing is launched
- *    and no cache state changes ([P1] 2.1: fail before the first layer); the
- *    message is available from gqa_last_error() on the calling thread.
+ *  - Every function returns a gqa_status.  On any error other than
+ *    GQA_ERR_HIP nothing is launched and no cache state changes ([P1] 2.1:
+ *    fail before the first layer); after GQA_ERR_HIP (a failed launch or copy)
+ *    the device contents are undefined.  The message is available from
+ *    gqa_last_error() on the calling thread.
  *  - Calls that take `stream` (a hipStream_t, NULL = legacy default stream)
  *    only enqueue work on it and return without synchronising.  All device
  *    buffers must stay alive until that work has completed.
@@ -147,12 +149,25 @@ gqa_status gqa_prefill(gqa_cache* cache, int32_t layer, int32_t B, const int32_t
                        const uint8_t* valid_mask, const int32_t* positions, const gqa_tensor* O,
                        void* workspace, size_t ws_bytes, void* stream);
 
+/* The attention half of gqa_prefill ([P1] 2.6 separates cache.write_sequence
+ * from causal_attention): for every valid query token, whose K/V must already
+ * be in the cache, at position p, O[b,h,i] attends to slots 0..p of layer
+ * `layer`.  The valid tokens of a row must carry consecutive positions
+ * p0, p0+1, ... that end at or before the layer's current length; rows of O
+ * for padding tokens are written as 0.  gqa_prefill is kv_cache_append
+ * followed by this call with p0 = the length before the append. */
+gqa_status gqa_attention(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
+                         const gqa_tensor* Q, const uint8_t* valid_mask, const int32_t* positions,
+                         const gqa_tensor* O, void* workspace, size_t ws_bytes, void* stream);
+
 /* Decode attention ([P2] decode shapes; [P3] single-token decode needs no mask):
  * one query per sequence at position T_b - 1 against all T_b cached slots of
  * layer `layer`.  valid_lengths (host int32 [B]) must equal each sequence's
  * current length in that layer (append the new token's K/V first) and be >= 1.
  * q and o are [B,Hq,1,d].  workspace: device scratch for split partials, at
- * least gqa_workspace_size(cache, B, Hq) bytes, 256-byte aligned. */
+ * least gqa_workspace_size(cache, B, Hq) bytes, 256-byte aligned; calls that
+ * share a workspace must not overlap in time.  It may be NULL when every
+ * sequence fits one split (short caches). */
 gqa_status gqa_decode(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
                       const gqa_tensor* q, const int32_t* valid_lengths, const gqa_tensor* o,
                       void* workspace, size_t ws_bytes, void* stream);
@@ -183,7 +198,8 @@ gqa_status gqa_cache_free_pages(const gqa_cache* cache, int32_t* out);
 gqa_status gqa_cache_check(const gqa_cache* cache);
 
 /* Device workspace bytes that suffice for gqa_decode with up to B sequences and
- * Hq query heads, whatever their lengths.  gqa_prefill needs none. */
+ * Hq query heads, whatever their lengths.  gqa_prefill and gqa_attention need
+ * none. */
 size_t gqa_workspace_size(const gqa_cache* cache, int32_t B, int32_t Hq);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -43,7 +43,7 @@ class Pair:
     def workspace(self, B, Hq):
         n = self.lib.gqa_workspace_size(self.gpu.handle, B, Hq)
         if self.ws is None or self.ws.numel() < n:
-            self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+            self.ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
         return self.ws
 
     # ------------------------------------------------------------ calls

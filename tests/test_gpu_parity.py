@@ -332,7 +332,7 @@ def test_serving_decode_full_size_sampled():
     lib.kv_cache_append(cache.handle, 0, list(range(B)), st.k.cuda(), st.v.cuda(),
                         torch.ones((B, 1), dtype=torch.uint8), torch.tensor([[x] for x in lens], dtype=torch.int32))
     o = torch.empty((B, 32, 1, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(lib.gqa_workspace_size(cache.handle, B, 32), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(lib.gqa_workspace_size(cache.handle, B, 32), dtype=torch.uint8, device="cuda")
     lib.gqa_decode(cache.handle, 0, list(range(B)), st.q.cuda(), [x + 1 for x in lens], o, ws)
     torch.cuda.synchronize()
     # block tables: a values-free run of the oracle's allocator with the same lengths
@@ -360,3 +360,73 @@ def test_serving_decode_full_size_sampled():
         assert np.array_equal(gk.float().numpy().view(np.uint32), ref.keys(0, 0).view(np.uint32))
         assert np.array_equal(gv.float().numpy().view(np.uint32), ref.values(0, 0).view(np.uint32))
     cache.close()
+
+
+def test_attention_half_matches_prefill():
+    say("case: kv_cache_append + gqa_attention == gqa_prefill; rows inside a cached sequence")
+    import causal_gqa_attention_attn_amd as lib
+    shape = W.AttnShape(B=2, n=170, Hq=32, Hkv=8, d=128, dtype=torch.bfloat16, theta=5e5)
+    inp = W.prefill_inputs(shape, 313, lengths=[170, 66])
+    a = Pair(1, 8, 128, 64, 2, 16, torch.bfloat16, 5e5)
+    O, _ = a.prefill(0, [0, 1], inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
+    b = Pair(1, 8, 128, 64, 2, 16, torch.bfloat16, 5e5)
+    b.append(0, [0, 1], inp.K, inp.V, inp.mask, inp.positions)
+    O2 = torch.full_like(O, float("nan"))
+    lib.gqa_attention(b.gpu.handle, 0, [0, 1], inp.Q.cuda(), inp.mask, inp.positions, O2)
+    torch.cuda.synchronize()
+    assert torch.equal(O.cpu().view(torch.int16), O2.cpu().view(torch.int16))
+    # 40 query rows at positions 100..139 of sequence 0, attending over its cached slots
+    Qm = inp.Q[0:1, :, 100:140].contiguous()
+    Om = torch.full_like(Qm, float("nan")).cuda()
+    lib.gqa_attention(b.gpu.handle, 0, [0], Qm.cuda(), torch.ones((1, 40), dtype=torch.uint8),
+                      torch.arange(100, 140, dtype=torch.int32)[None], Om)
+    torch.cuda.synchronize()
+    ref = b.ref.prefill_rows(0, 0, as_f32(Qm[0]), list(range(100, 140)))
+    compare_rows(Om[0], ref, torch.bfloat16)
+    with pytest.raises(lib.GqaError) as e:   # queries beyond the cached length
+        lib.gqa_attention(b.gpu.handle, 0, [1], Qm.cuda(), torch.ones((1, 40), dtype=torch.uint8),
+                          torch.arange(50, 90, dtype=torch.int32)[None], Om)
+    assert e.value.name == "POSITION"
+
+
+def test_decode_graph_replay_matches_eager():
+    say("case: HIP-graph replay of append + decode equals the eager calls, replay after replay")
+    import causal_gqa_attention_attn_amd as lib
+    N, L = 700, 3
+    c = lib.PagedCache(L, 8, 128, 64, 1, 64, dtype=torch.bfloat16, rope_theta=1e4, max_position=1024)
+    for l in range(L):
+        lib.kv_cache_append(c.handle, l, [0], W.normal_device((1, 8, N - 1, 128), 10 + l),
+                            W.normal_device((1, 8, N - 1, 128), 20 + l), torch.ones((1, N - 1), dtype=torch.uint8),
+                            torch.arange(N - 1, dtype=torch.int32)[None])
+    q = [W.normal_device((1, 48, 1, 128), 30 + l) for l in range(L)]
+    k = [W.normal_device((1, 8, 1, 128), 40 + l) for l in range(L)]
+    v = [W.normal_device((1, 8, 1, 128), 50 + l) for l in range(L)]
+    o = [torch.empty_like(x) for x in q]
+    ws = torch.zeros(lib.gqa_workspace_size(c.handle, 1, 48), dtype=torch.uint8, device="cuda")
+    one = torch.ones((1, 1), dtype=torch.uint8)
+    pn = torch.tensor([[N - 1]], dtype=torch.int32)
+
+    def run():
+        for l in range(L):
+            lib.kv_cache_append(c.handle, l, [0], k[l], v[l], one, pn)
+            lib.gqa_decode(c.handle, l, [0], q[l], [N], o[l], ws)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in o]
+    for l in range(L):
+        lib.kv_cache_truncate(c.handle, 0, N - 1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    lib.kv_cache_truncate(c.handle, 0, N - 1)
+    for rep in range(3):
+        for x in o:
+            x.fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device="cuda") * 2     # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        del scratch
+        for a, b in zip(o, eager):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}"
+    c.close()
