@@ -8,28 +8,40 @@
 // prefill of page "KV Cache 与 Prefill/Decode 推理路径": the prefix is wholly
 // visible, the new block lower-triangular).  Padding rows of O are zeroed.
 //
-// How (gfx950 design, not a translation of any page's kernel):
-//  * one workgroup = (kv head g, up to 8 query heads of its group, sequence,
-//    32 query tokens); one wave per query head, so every K/V tile staged in LDS
-//    is shared by all query heads of the group (the head map is an index, the
-//    cache is never replicated);
+// How (a gfx950 design, not a translation of any page's kernel):
+//  * one workgroup = 4 waves, one per SIMD, for (kv head g, a chunk of Gc of
+//    its query heads, sequence, Tq query tokens).  Its Gc*Tq query rows form
+//    row-blocks of 32 (one head, 32 tokens); each wave owns R of them, so every
+//    K/V fragment it reads from LDS feeds R matrix-core products, and every K/V
+//    tile staged in LDS serves all Gc query heads of the group (the head map is
+//    an index; the cache is never replicated);
 //  * S^T = K q^T on v_mfma_f32_32x32x16_bf16 with keys as rows: each lane owns
-//    one query column, so row max and row sum stay inside a lane plus one
-//    exchange with the lane 32 away;
-//  * K rows are fed to the matrix core in a fixed permutation so that the score
+//    one query column, so row maxima and sums stay in a lane plus one exchange
+//    with the lane 32 away;
+//  * K rows are fed to the matrix core in a fixed permutation so the score
 //    accumulator already has the register layout of the B operand of
-//    O^T += V^T P^T (no shuffle of P);
-//  * V pages are stored d-major, so V^T tiles are staged with plain 16-byte
-//    copies;
-//  * online softmax in base 2 with the 1/sqrt(d)*log2(e) scale folded into one
-//    multiply-add; the running maximum starts at a finite sentinel so a tile in
-//    which every key is masked never evaluates (-inf) - (-inf);
-//  * key tiles wholly in the future of the block are never loaded (the loop
-//    ends at the block's last query position); only tiles crossing the
-//    diagonal are masked, by select;
+//    O^T += V^T P^T (no shuffle of P); V pages are stored d-major, so V^T tiles
+//    are staged with plain 16-byte copies;
+//  * 64-key K/V tiles are double-buffered in LDS: the next tile's global loads
+//    are in flight while the current one is used, one barrier per tile;
+//  * softmax in base 2 with the 1/sqrt(d)*log2(e) scale folded into one
+//    multiply-add, against a fixed reference per query row: the maximum of the
+//    row's first 32-key sub-tile (which always holds key 0, visible to every
+//    query, so the reference is finite and a fully masked later tile never
+//    meets (-inf) - (-inf)).  Unnormalised probabilities 2^(s - ref) and their
+//    sums stay exact in float32/bf16 range while no score exceeds the
+//    reference by more than 2^64, so the output accumulators are never
+//    rescaled in the loop.  Each lane records its largest score; if any lane
+//    of the workgroup passes that bound, the workgroup runs the tile loop once
+//    more with the recorded maxima as references, which cannot overflow;
+//  * key tiles wholly in the future of a workgroup are never loaded; 32-key
+//    sub-tiles wholly in the future of a row-block are skipped; masking by
+//    select happens only on tiles that cross the diagonal;
 //  * slots at or beyond the written length are zero-filled in LDS, so stale or
 //    poisoned cache memory never meets a zero weight (0 * NaN);
-//  * blocks are dispatched heaviest (last) query tile first.
+//  * workgroups are dispatched heaviest (last) query tile first.
+#include <type_traits>
+
 #include "common.hpp"
 #include "device.hpp"
 
@@ -43,80 +55,106 @@ __device__ __forceinline__ int perm32(int r) {
   return ((r >> 4) << 4) + (((r >> 2) & 1) << 3) + (((r >> 3) & 1) << 2) + (r & 3);
 }
 
-}  // namespace
+constexpr int KT = 64;                 // keys per staged tile
 
 template <int D>
-__global__ __launch_bounds__(512) void prefill_bf16_kernel(AttnArgs a) {
-  constexpr int KT = 64;          // keys per staged tile
-  constexpr int KPAD = D + 8;     // LDS row stride of K (elements)
-  constexpr int VPAD = KT + 8;    // LDS row stride of V^T
-  constexpr int NC = D / 16;      // k-steps of the score product
-  constexpr int NDB = D / 32;     // 32-row blocks of the output
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[KT * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * VPAD];
+struct Smem {
+  static constexpr int KPAD = D + 8;   // LDS row stride of K (elements)
+  static constexpr int VPAD = KT + 8;  // LDS row stride of V^T
+  static constexpr int K_ELEMS = KT * KPAD;
+  static constexpr int V_ELEMS = D * VPAD;
+  static constexpr int BUF = K_ELEMS + V_ELEMS;
+};
+
+}  // namespace
+
+// Template R: row-blocks per wave.  Runtime Gc (heads per workgroup) and TB
+// (32-token blocks per workgroup) satisfy Gc * TB == 4 * R.
+template <int D, int R>
+__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(AttnArgs a, int Gc, int TB) {
+  using S = Smem<D>;
+  constexpr int NC = D / 16;           // k-steps of the score product
+  constexpr int NDB = D / 32;          // 32-row blocks of the output
+  constexpr int KCH = KT * D / 8;      // 16-byte chunks of a K (or V) tile
+  constexpr int PER_T = KCH / 256;     // chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * S::BUF];
 
   const int G = a.Hq / a.Hkv;
-  const int chunks = (G + 7) >> 3;
-  const int g = blockIdx.x / chunks;
-  const int hc = blockIdx.x - g * chunks;
+  const int nchunk = G / Gc;
+  const int g = blockIdx.x / nchunk;
+  const int hc = blockIdx.x - g * nchunk;
   const int b = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
+  const int Tq = 32 * TB;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int heads_here = min(8, G - hc * 8);
-  const bool active = wave < heads_here;
-  const int h = g * G + hc * 8 + wave;
 
   const int seq = a.meta.seq[b];
   const int c0 = a.meta.start[b];
   const int nb = a.meta.count[b];
   const int r0 = a.meta.row0[b];
   const int total = a.meta.total[b];
+  const int h0 = g * G + hc * Gc;      // first query head of this workgroup
 
-  uint16_t* obase = static_cast<uint16_t*>(a.O) + b * a.o_s0 + static_cast<int64_t>(h) * a.o_s1;
-
-  // padding rows of this block's rectangular range -> 0
-  if (active) {
-    const int rlo = tile * 32;
-    const int rhi = min(a.n_rect, rlo + 32);
-    for (int idx = lane; idx < 32 * (D / 8); idx += 64) {
-      const int rr = rlo + idx / (D / 8);
-      const int ch = idx % (D / 8);
+  // padding rows of this workgroup's rectangular range -> 0
+  {
+    const int rlo = tile * Tq;
+    const int rhi = min(a.n_rect, rlo + Tq);
+    const int per_row = D / 8;
+    for (int idx = threadIdx.x; idx < Gc * Tq * per_row; idx += 256) {
+      const int hh = idx / (Tq * per_row);
+      const int rem = idx - hh * Tq * per_row;
+      const int rr = rlo + rem / per_row;
+      const int ch = rem % per_row;
       if (rr < rhi && (rr < r0 || rr >= r0 + nb)) {
         const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(obase + static_cast<int64_t>(rr) * a.o_s2 + ch * 8) = z;
+        uint16_t* op = static_cast<uint16_t*>(a.O) + b * a.o_s0 + static_cast<int64_t>(h0 + hh) * a.o_s1 +
+                       static_cast<int64_t>(rr) * a.o_s2 + ch * 8;
+        *reinterpret_cast<u32x4*>(op) = z;
       }
     }
   }
 
-  const int t0 = tile * 32;
+  const int t0 = tile * Tq;
   if (t0 >= nb) return;
-  const int qn = min(32, nb - t0);
-  const bool qvalid = col < qn;
-  const int pos = c0 + t0 + col;
+  const int qn = min(Tq, nb - t0);
+
+  // this wave's row-blocks: head, first token, validity
+  int rb_h[R], rb_t[R];
+  bool rb_ok[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int rb = wave * R + j;
+    rb_h[j] = h0 + rb / TB;
+    rb_t[j] = (rb % TB) * 32;          // token offset inside the tile
+    rb_ok[j] = rb_t[j] < qn;
+  }
 
   // rotated queries as B operands: lane holds dims 16c + 8*half + 0..7 of its query
-  bf16x8 qf[NC];
-  if (active) {
+  bf16x8 qf[R][NC];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int t = t0 + rb_t[j] + col;
+    const bool qv = rb_ok[j] && (rb_t[j] + col < qn);
     float x[NC][8];
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.q_s0 + static_cast<int64_t>(h) * a.q_s1 +
-                           static_cast<int64_t>(r0 + t0 + col) * a.q_s2;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.q_s0 + static_cast<int64_t>(rb_h[j]) * a.q_s1 +
+                           static_cast<int64_t>(r0 + t) * a.q_s2;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qvalid) w = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
+      if (qv) w = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[c][2 * e] = __uint_as_float(w[e] << 16);
         x[c][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
       }
     }
-    if (a.rope && qvalid) {
-      const float* rrow = a.rope + static_cast<int64_t>(pos) * D;   // (D/2) pairs
+    if (a.rope && qv) {
+      const float* rrow = a.rope + static_cast<int64_t>(c0 + t) * D;    // (D/2) (cos, sin) pairs
 #pragma unroll
-      for (int c = 0; c < NC / 2; ++c) {
+      for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = c * 16 + half * 8 + e;
@@ -125,161 +163,273 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(AttnArgs a) {
           x[c][e] = lo;
           x[c + NC / 2][e] = hi;
         }
-      }
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[c][2 * e], x[c][2 * e + 1]);
-      qf[c] = __builtin_bit_cast(bf16x8, w);
+      qf[j][c] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
   const int kv_end = c0 + t0 + qn;            // keys [0, kv_end) can be visible
   const int ntk = (kv_end + KT - 1) / KT;
-  const int diag = c0 + t0;                   // smallest query position of the block
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
   const int32_t* trow = a.table + static_cast<int64_t>(seq) * a.table_w;
   const int Hkv = a.Hkv;
   const float sl2 = a.scale_log2;
 
-  f32x16 o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_run = -1e30f;     // finite sentinel (log2 units)
-  float l_run = 0.f;
-  const int krow_l = perm32(col);
-
-  for (int kt = 0; kt < ntk; ++kt) {
+  // ---- global -> registers -> LDS staging of one K/V tile.  The tile's
+  // four pages are looked up once; a thread's 16-byte chunks fall in known
+  // pages, so all its loads issue back to back.  Slots at or past the written
+  // length read a valid page and are zeroed afterwards (no branches).
+  const int last_page = (total - 1) >> 4;
+  u32x4 stg[2 * PER_T];
+  auto load_tile = [&](int kt) {
     const int kbase = kt * KT;
-    __syncthreads();
-    for (int ci = threadIdx.x; ci < KT * D / 8; ci += blockDim.x) {
+    int64_t phys[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) phys[p] = trow[min(kt * 4 + p, last_page)];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int ci = threadIdx.x + 256 * i;
       const int kl = ci / (D / 8);
       const int ch = ci - kl * (D / 8);
-      const int key = kbase + kl;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (key < total) {
-        const int64_t phys = trow[key >> 4];
-        val = *reinterpret_cast<const u32x4*>(kpool + ((phys * Hkv + g) * kPage + (key & 15)) * D + ch * 8);
-      }
-      *reinterpret_cast<u32x4*>(k_lds + kl * KPAD + ch * 8) = val;
+      const int pl = kl >> 4;
+      const int64_t ph = pl == 0 ? phys[0] : pl == 1 ? phys[1] : pl == 2 ? phys[2] : phys[3];
+      stg[i] = *reinterpret_cast<const u32x4*>(kpool + ((ph * Hkv + g) * kPage + (kl & 15)) * D + ch * 8);
     }
-    for (int ci = threadIdx.x; ci < KT * D / 8; ci += blockDim.x) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int ci = threadIdx.x + 256 * i;
       const int pl = ci / (D * 2);
       const int rem = ci - pl * (D * 2);
       const int dd = rem >> 1;
       const int h8 = rem & 1;
-      const int key0 = kbase + pl * 16 + h8 * 8;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (key0 < total) {
-        const int64_t phys = trow[key0 >> 4];
-        val = *reinterpret_cast<const u32x4*>(vpool + ((phys * Hkv + g) * D + dd) * kPage + h8 * 8);
-        const int nv = total - key0;
-        if (nv < 8) {
+      const int64_t ph = pl == 0 ? phys[0] : pl == 1 ? phys[1] : pl == 2 ? phys[2] : phys[3];
+      stg[PER_T + i] = *reinterpret_cast<const u32x4*>(vpool + ((ph * Hkv + g) * D + dd) * kPage + h8 * 8);
+    }
+    if (kbase + KT > total) {            // the tile holds the end of the sequence
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t keep_lo = (2 * e < nv) ? 0x0000ffffu : 0u;
-            const uint32_t keep_hi = (2 * e + 1 < nv) ? 0xffff0000u : 0u;
-            val[e] &= (keep_lo | keep_hi);
+      for (int i = 0; i < PER_T; ++i) {
+        const int ci = threadIdx.x + 256 * i;
+        const int key = kbase + ci / (D / 8);
+        if (key >= total) stg[i] = u32x4{0u, 0u, 0u, 0u};
+        const int pl = ci / (D * 2);
+        const int h8 = (ci - pl * (D * 2)) & 1;
+        const int key0 = kbase + pl * 16 + h8 * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t keep_lo = (key0 + 2 * e < total) ? 0x0000ffffu : 0u;
+          const uint32_t keep_hi = (key0 + 2 * e + 1 < total) ? 0xffff0000u : 0u;
+          stg[PER_T + i][e] &= (keep_lo | keep_hi);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* kl_s = smem + buf * S::BUF;
+    uint16_t* vl_s = kl_s + S::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int ci = threadIdx.x + 256 * i;
+      const int kl = ci / (D / 8);
+      const int ch = ci - kl * (D / 8);
+      *reinterpret_cast<u32x4*>(kl_s + kl * S::KPAD + ch * 8) = stg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int ci = threadIdx.x + 256 * i;
+      const int pl = ci / (D * 2);
+      const int rem = ci - pl * (D * 2);
+      const int dd = rem >> 1;
+      const int h8 = rem & 1;
+      *reinterpret_cast<u32x4*>(vl_s + dd * S::VPAD + pl * 16 + h8 * 8) = stg[PER_T + i];
+    }
+  };
+
+  f32x16 o[R][NDB];
+  float m_ref[R], m_seen[R], l_run[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    m_ref[j] = -INFINITY;              // set from the first sub-tile of the row-block
+    m_seen[j] = -INFINITY;
+  }
+  const int krow_l = perm32(col);
+  bool all_ok = true;
+#pragma unroll
+  for (int j = 0; j < R; ++j) all_ok = all_ok && rb_ok[j];
+  bool ovf = false;
+  int pass = 0;
+  __shared__ int redo;
+  auto compute_tile = [&](const uint16_t* kl_s, const uint16_t* vl_s, int kt, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+        const int k0 = kt * KT + sub * 32;
+        bool act[R];
+        bool msk[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int qlo = c0 + t0 + rb_t[j];           // smallest query position of the row-block
+          act[j] = MASKED ? (rb_ok[j] && k0 <= qlo + 31) : true;
+          msk[j] = MASKED && k0 + 31 > qlo;
+        }
+        // S^T for 32 keys and each active row-block
+        f32x16 sc[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[j][i] = 0.f;
+        const uint16_t* kr = kl_s + (sub * 32 + krow_l) * S::KPAD + half * 8;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + c * 16);
+#pragma unroll
+          for (int j = 0; j < R; ++j)
+            if (act[j]) sc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], sc[j], 0, 0, 0);
+        }
+        bf16x8 pf[R][2];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          if (!act[j]) continue;
+          if (msk[j]) {
+            const int pos = c0 + t0 + rb_t[j] + col;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = k0 + 16 * (i >> 3) + 8 * half + (i & 7);
+              if (key > pos) sc[j][i] = -INFINITY;
+            }
           }
+          float mx = sc[j][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[j][i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+          if (pass == 0 && k0 == 0) m_ref[j] = mx;    // first sub-tile of every row-block
+          m_seen[j] = fmaxf(m_seen[j], mx);
+          ovf |= mx > m_ref[j] + 64.f;
+          const float mneg = -m_ref[j];
+          float lsum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[j][i], sl2, mneg));
+            lsum += p;
+            pf[j][i >> 3][i & 7] = static_cast<__bf16>(p);
+          }
+          l_run[j] += lsum;
         }
+        // O^T += V^T P^T for the 32 keys (two 16-key k-blocks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+                vl_s + (db * 32 + krow_l) * S::VPAD + sub * 32 + kb * 16 + half * 8);
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+              if (act[j]) o[j][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][kb], o[j][db], 0, 0, 0);
+          }
       }
-      *reinterpret_cast<u32x4*>(v_lds + dd * VPAD + pl * 16 + h8 * 8) = val;
+  };
+
+  for (pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[j][db][i] = 0.f;
+      l_run[j] = 0.f;
     }
+    ovf = false;
+    load_tile(0);
+    store_tile(0);
     __syncthreads();
-    if (!active) continue;
 
-    // S^T for 64 keys: two 32-key blocks
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const uint16_t* kr = k_lds + (kb * 32 + krow_l) * KPAD + half * 8;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + c * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+    for (int kt = 0; kt < ntk; ++kt) {
+      const bool more = kt + 1 < ntk;
+      if (more) load_tile(kt + 1);
+      const uint16_t* kl_s = smem + (kt & 1) * S::BUF;
+      const uint16_t* vl_s = kl_s + S::K_ELEMS;
+      // tiles wholly at or below every row-block's smallest query position need
+      // neither masks nor activity checks
+      if (kt * KT + KT - 1 <= c0 + t0 && all_ok) {
+        compute_tile(kl_s, vl_s, kt, std::integral_constant<bool, false>());
+      } else {
+        compute_tile(kl_s, vl_s, kt, std::integral_constant<bool, true>());
       }
+      if (more) store_tile((kt + 1) & 1);
+      __syncthreads();
     }
-    if (kbase + KT - 1 > diag) {
+    // does any lane of the workgroup need a second pass?
+    if (threadIdx.x == 0) redo = 0;
+    __syncthreads();
+    if (__any(ovf) && lane == 0) redo = 1;
+    __syncthreads();
+    if (!redo) break;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + kb * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
-          if (key > pos) s[kb][i] = -INFINITY;
-        }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    bf16x8 pf[2][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], sl2, -m_new));
-        lsum += p;
-        pf[kb][i >> 3][i & 7] = static_cast<__bf16>(p);
-      }
-    l_run += lsum;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-              v_lds + (db * 32 + krow_l) * VPAD + kb * 32 + sub * 16 + half * 8);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][sub], o[db], 0, 0, 0);
-        }
+    for (int j = 0; j < R; ++j) m_ref[j] = m_seen[j];
+    __syncthreads();
   }
 
-  if (!active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
-  if (qvalid) {
-    uint16_t* orow = obase + static_cast<int64_t>(r0 + t0 + col) * a.o_s2;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int j = 0; j < R; ++j) {
+    const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
+    const float inv = 1.f / l_tot;
+    if (rb_ok[j] && rb_t[j] + col < qn) {
+      uint16_t* orow = static_cast<uint16_t*>(a.O) + b * a.o_s0 + static_cast<int64_t>(rb_h[j]) * a.o_s1 +
+                       static_cast<int64_t>(r0 + t0 + rb_t[j] + col) * a.o_s2;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        u32x4 w;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = pack_bf16x2(o[db][sub * 8 + 2 * e] * inv, o[db][sub * 8 + 2 * e + 1] * inv);
-        *reinterpret_cast<u32x4*>(orow + db * 32 + sub * 16 + half * 8) = w;
-      }
+        for (int kb = 0; kb < 2; ++kb) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = pack_bf16x2(o[j][db][kb * 8 + 2 * e] * inv, o[j][db][kb * 8 + 2 * e + 1] * inv);
+          *reinterpret_cast<u32x4*>(orow + db * 32 + kb * 16 + half * 8) = w;
+        }
+    }
   }
+}
+
+// Heads per workgroup (Gc, dividing G) and 32-token blocks per workgroup (TB)
+// with Gc * TB = 4 * R: three row-blocks per wave when the group size allows,
+// else two, else one.
+struct PrefillShape {
+  int Gc, TB, R;
+};
+
+#ifndef GQA_PREFILL_MAX_R
+#define GQA_PREFILL_MAX_R 3
+#endif
+
+static PrefillShape prefill_shape(int G) {
+  for (int R = GQA_PREFILL_MAX_R; R >= 1; --R)
+    for (int Gc = G; Gc >= 1; --Gc)
+      if (G % Gc == 0 && (4 * R) % Gc == 0) return {Gc, 4 * R / Gc, R};
+  return {1, 4, 1};
 }
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const int chunks = (G + 7) / 8;
-  const int waves = G < 8 ? G : 8;
-  dim3 grid(a.Hkv * chunks, a.nseq, (a.n_rect + 31) / 32);
-  dim3 block(64 * waves);
-  if (a.d == 128)
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, s, a);
+  const PrefillShape ps = prefill_shape(G);
+  const int Tq = 32 * ps.TB;
+  dim3 grid(a.Hkv * (G / ps.Gc), a.nseq, (a.n_rect + Tq - 1) / Tq);
+  dim3 block(256);
+#define GQA_LAUNCH(DD, RR) hipLaunchKernelGGL((prefill_bf16_kernel<DD, RR>), grid, block, 0, s, a, ps.Gc, ps.TB)
+  if (a.d == 128) {
+    if (ps.R == 3) GQA_LAUNCH(128, 3);
+    else if (ps.R == 2) GQA_LAUNCH(128, 2);
+    else GQA_LAUNCH(128, 1);
+  } else {
+    if (ps.R == 3) GQA_LAUNCH(64, 3);
+    else if (ps.R == 2) GQA_LAUNCH(64, 2);
+    else GQA_LAUNCH(64, 1);
+  }
+#undef GQA_LAUNCH
   return hipGetLastError();
 }
 
