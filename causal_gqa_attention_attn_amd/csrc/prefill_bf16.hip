@@ -71,7 +71,7 @@ struct Smem {
 // Template R: row-blocks per wave.  Runtime Gc (heads per workgroup) and TB
 // (32-token blocks per workgroup) satisfy Gc * TB == 4 * R.
 template <int D, int R>
-__global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(AttnArgs a, int Gc, int TB) {
+__global__ __launch_bounds__(256, R == 1 ? 2 : 1) void prefill_bf16_kernel(AttnArgs a, int Gc, int TB) {
   using S = Smem<D>;
   constexpr int NC = D / 16;           // k-steps of the score product
   constexpr int NDB = D / 32;          // 32-row blocks of the output
@@ -264,20 +264,97 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(AttnArgs a, int Gc
   bool ovf = false;
   int pass = 0;
   __shared__ int redo;
+  // softmax of one 32-key sub-tile for row-block j: mask, row maximum,
+  // probabilities against the row's reference, row sum, bf16 B operands
+  auto softmax32 = [&](f32x16& sc, int j, int k0, bool msk, bf16x8* pf) {
+    if (msk) {
+      const int pos = c0 + t0 + rb_t[j] + col;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 16 * (i >> 3) + 8 * half + (i & 7);
+        if (key > pos) sc[i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
+    mx = fmaxf(mx, sc[15]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    if (pass == 0 && k0 == 0) m_ref[j] = mx;      // first sub-tile of every row-block
+    m_seen[j] = fmaxf(m_seen[j], mx);
+    ovf |= mx > m_ref[j] + 64.f;
+    const float mneg = -m_ref[j];
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, mneg));
+      lsum += p;
+      pf[i >> 3][i & 7] = static_cast<__bf16>(p);
+    }
+    l_run[j] += lsum;
+  };
+
   auto compute_tile = [&](const uint16_t* kl_s, const uint16_t* vl_s, int kt, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
+    if constexpr (R == 1) {
+      // both 32-key sub-tiles at once: two independent accumulator chains
+      const int qlo = c0 + t0 + rb_t[0];
+      bool act[2], msk[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < 2; ++sub) {
+        const int k0 = kt * KT + sub * 32;
+        act[sub] = MASKED ? (rb_ok[0] && k0 <= qlo + 31) : true;
+        msk[sub] = MASKED && k0 + 31 > qlo;
+      }
+      f32x16 sc[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[sub][i] = 0.f;
+      const uint16_t* kr = kl_s + krow_l * S::KPAD + half * 8;
+      if (!MASKED || act[1]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kr + c * 16);
+          const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(kr + 32 * S::KPAD + c * 16);
+          sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0][c], sc[0], 0, 0, 0);
+          sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[0][c], sc[1], 0, 0, 0);
+        }
+      } else if (act[0]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kr + c * 16);
+          sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0][c], sc[0], 0, 0, 0);
+        }
+      }
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+        if (!MASKED || act[sub]) softmax32(sc[sub], 0, kt * KT + sub * 32, msk[sub], pf[sub]);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        if (MASKED && !act[sub]) continue;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+                vl_s + (db * 32 + krow_l) * S::VPAD + sub * 32 + kb * 16 + half * 8);
+            o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[sub][kb], o[0][db], 0, 0, 0);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
         const int k0 = kt * KT + sub * 32;
         bool act[R];
         bool msk[R];
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-          const int qlo = c0 + t0 + rb_t[j];           // smallest query position of the row-block
+          const int qlo = c0 + t0 + rb_t[j];         // smallest query position of the row-block
           act[j] = MASKED ? (rb_ok[j] && k0 <= qlo + 31) : true;
           msk[j] = MASKED && k0 + 31 > qlo;
         }
-        // S^T for 32 keys and each active row-block
         f32x16 sc[R];
 #pragma unroll
         for (int j = 0; j < R; ++j)
@@ -293,34 +370,8 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(AttnArgs a, int Gc
         }
         bf16x8 pf[R][2];
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-          if (!act[j]) continue;
-          if (msk[j]) {
-            const int pos = c0 + t0 + rb_t[j] + col;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 16 * (i >> 3) + 8 * half + (i & 7);
-              if (key > pos) sc[j][i] = -INFINITY;
-            }
-          }
-          float mx = sc[j][0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[j][i]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-          if (pass == 0 && k0 == 0) m_ref[j] = mx;    // first sub-tile of every row-block
-          m_seen[j] = fmaxf(m_seen[j], mx);
-          ovf |= mx > m_ref[j] + 64.f;
-          const float mneg = -m_ref[j];
-          float lsum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[j][i], sl2, mneg));
-            lsum += p;
-            pf[j][i >> 3][i & 7] = static_cast<__bf16>(p);
-          }
-          l_run[j] += lsum;
-        }
-        // O^T += V^T P^T for the 32 keys (two 16-key k-blocks)
+        for (int j = 0; j < R; ++j)
+          if (act[j]) softmax32(sc[j], j, k0, msk[j], pf[j]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -332,6 +383,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bf16_kernel(AttnArgs a, int Gc
               if (act[j]) o[j][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][kb], o[j][db], 0, 0, 0);
           }
       }
+    }
   };
 
   for (pass = 0; pass < 2; ++pass) {
@@ -403,7 +455,7 @@ struct PrefillShape {
 };
 
 #ifndef GQA_PREFILL_MAX_R
-#define GQA_PREFILL_MAX_R 3
+#define GQA_PREFILL_MAX_R 1
 #endif
 
 static PrefillShape prefill_shape(int G) {

@@ -430,3 +430,19 @@ def test_decode_graph_replay_matches_eager():
         for a, b in zip(o, eager):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}"
     c.close()
+
+
+def test_prefill_second_pass_on_score_overflow():
+    say("case: a late key whose score dwarfs the first tile's maximum (forces the prefill's second pass)")
+    shape = W.AttnShape(B=1, n=200, Hq=8, Hkv=2, d=128, dtype=torch.bfloat16, theta=0.0)
+    inp = W.prefill_inputs(shape, 901)
+    # key 150 of kv head 0 and every query of heads 0..3 point the same way with large norm
+    direction = torch.zeros(128)
+    direction[3] = 1.0
+    inp.K[0, 0, 150] = (40.0 * direction).to(torch.bfloat16)
+    inp.Q[0, :4, 120:] = (40.0 * direction).to(torch.bfloat16)
+    pair = Pair(1, 2, 128, 16, 1, 16, torch.bfloat16, 0.0)
+    O, ref = pair.prefill(0, [0], inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+    compare_rows(O, ref, torch.bfloat16)
+    # rows after the spike are dominated by it: their output is value row 150
+    assert torch.allclose(O[0, 0, 160].float().cpu(), inp.V[0, 0, 150].float(), atol=1e-2)
