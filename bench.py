@@ -76,7 +76,9 @@ def cpu_baseline(inp, budget_s):
     Q = inp.Q.float().numpy()
     m = CacheModel(1, HKV, D, 16, N // 16, 1, N // 16, dtype="bf16", rope_theta=THETA, max_position=N)
     m.append(0, [0], K, V, np.ones((1, N), np.uint8), np.arange(N)[None])
-    blocks = list(range(N - 64, -1, -N // 16))      # 16 blocks, heaviest first
+    # all 64-row blocks, interleaved so that any prefix of the list is spread over
+    # the sequence (heaviest first within each sweep)
+    blocks = [r0 for off in range(16) for r0 in range(N - 64 - 64 * off, -1, -1024)]
     rows_done, flops, t_used = 0, 0.0, 0.0
     for r0 in blocks:
         rows = list(range(r0, r0 + 64))
@@ -100,6 +102,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (profiling aid)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 256 MiB device-to-device 5 times (calibrates rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -112,6 +116,14 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda"
+    if args.copy_probe:
+        src = torch.full((256 << 20,), 1, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_per_copy": 256 << 20, "copies": 5}), flush=True)
+        return
     print("bench: generating inputs", file=sys.stderr, flush=True)
     inp = W.grok()
     Q, K, V = inp.Q.to(dev), inp.K.to(dev), inp.V.to(dev)
@@ -216,8 +228,8 @@ def main():
                    "causal_flops": flops, "causal_flops_exact": 2.0 * HQ * D * N * (N + 1)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic("prefill_bf16_kernel<128>", src_prefill),
-                     "kernel": "prefill_bf16_kernel<128>"},
+                     "traffic": _traffic("prefill_bf16_kernel<128, 1>", src_prefill),
+                     "kernel": "prefill_bf16_kernel<128, 1>"},
     }
     if not args.prefill_only:
         span_ms = mean([e[3].elapsed_time(e[4]) for e in events])
