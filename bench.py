@@ -7,9 +7,9 @@ One step = one pass of the whole path over one batch of synthetic input:
     kv_cache_append (validation, page reservation, block-table patch, fused
     rotation + paged cache write) then gqa_attention (the MFMA causal kernel);
     together these are exactly gqa_prefill;
-  * decode at T=8192 over a 64-layer bf16 cache: per layer kv_cache_append of
-    the new token (position 8191) and gqa_decode of one query reading all 8192
-    slots (2^31 bytes of K/V over the 64 layers).  The 64-layer loop is captured
+  * decode at T=8192 over a 64-layer bf16 cache: per layer gqa_decode_step,
+    which appends the new token (position 8191) and decodes one query reading
+    all 8192 slots, in one launch (2^31 bytes of K/V over the 64 layers).  The 64-layer loop is captured
     once as a HIP graph and replayed, so every step does the same work.
 
 Inputs are resident in HBM before the timed region.  ``value`` is the causal
@@ -155,8 +155,7 @@ def main():
 
     def decode_layers():
         for l in range(LAYERS):
-            lib.kv_cache_append(dec.handle, l, [0], kd[l], vd[l], one, p_new)
-            lib.gqa_decode(dec.handle, l, [0], qd[l], [N], od[l], ws)
+            lib.gqa_decode_step(dec.handle, l, [0], qd[l], kd[l], vd[l], od[l], ws)
 
     # The 64-layer decode loop is launch-bound from Python (two library calls per
     # layer), so it is captured once in a HIP graph and replayed: every replay
@@ -238,13 +237,13 @@ def main():
         achieved = kv_bytes / LAYERS / (per_layer_ms * 1e-3) / 1e9
         out["decode"] = {"value": round(kv_bytes / (span_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                          "kv_bytes_per_step": kv_bytes, "ms_64_layers": round(span_ms, 4),
-                         "note": "64 x (append of the new token + decode at T=8192), replayed as one HIP graph"}
+                         "note": "64 x gqa_decode_step (append of the new token + decode at T=8192, one launch each), replayed as one HIP graph"}
         src_dec = os.path.join(ROOT, "causal_gqa_attention_attn_amd", "csrc", "decode_bf16.hip")
         out["roofline_decode"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                                   "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                                   "traffic": _traffic("decode_bf16_kernel<128>", src_dec),
-                                  "kernel": "one layer of the replayed decode graph: append + decode_bf16_kernel<128> "
-                                            "+ decode_merge_kernel<128>, 32 MiB of K/V",
+                                  "kernel": "one layer of the replayed decode graph: decode_bf16_kernel<128> "
+                                            "(append, split-T attention and split combine), 32 MiB of K/V",
                                   "layer_us": round(per_layer_ms * 1e3, 2)}
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -32,7 +32,7 @@ F32, BF16 = 0, 1
 STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "MASK", -5: "POSITION",
           -6: "CACHE", -7: "OUT_OF_PAGES", -8: "UNSUPPORTED", -9: "HIP"}
 EXPORTS = ["gqa_cache_buffer_sizes", "gqa_cache_create", "gqa_cache_destroy", "kv_cache_append",
-           "gqa_prefill", "gqa_attention", "gqa_decode", "kv_cache_truncate", "kv_cache_remap", "gqa_cache_length",
+           "gqa_prefill", "gqa_attention", "gqa_decode", "gqa_decode_step", "kv_cache_truncate", "kv_cache_remap", "gqa_cache_length",
            "gqa_cache_page_table", "gqa_cache_free_pages", "gqa_cache_check", "gqa_workspace_size",
            "gqa_last_error"]
 
@@ -72,6 +72,7 @@ _sig = {
                     ctypes.c_size_t, _P],
     "gqa_attention": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _P, _P, _TP, _P, ctypes.c_size_t, _P],
     "gqa_decode": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _P, _TP, _P, ctypes.c_size_t, _P],
+    "gqa_decode_step": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _TP, _TP, _TP, _P, ctypes.c_size_t, _P],
     "kv_cache_truncate": [_P, ctypes.c_int32, ctypes.c_int32],
     "kv_cache_remap": [_P, ctypes.c_int32, _P, _P, _P],
     "gqa_cache_length": [_P, ctypes.c_int32, ctypes.c_int32, _I32P],
@@ -203,6 +204,15 @@ def gqa_decode(handle, layer, seq_ids, q, valid_lengths, o, workspace=None, stre
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.gqa_decode(handle, layer, len(ids), _ptr(ids), ctypes.byref(tq), _ptr(lens),
                            ctypes.byref(to), ws, nbytes, _stream(stream)), "gqa_decode")
+
+
+def gqa_decode_step(handle, layer, seq_ids, q, k_new, v_new, o, workspace=None, stream=None):
+    ids = _host_i32(seq_ids)
+    tq, tk, tv, to = _tensor(q), _tensor(k_new), _tensor(v_new), _tensor(o)
+    ws = None if workspace is None else workspace.data_ptr()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.gqa_decode_step(handle, layer, len(ids), _ptr(ids), ctypes.byref(tq), ctypes.byref(tk),
+                                ctypes.byref(tv), ctypes.byref(to), ws, nbytes, _stream(stream)), "gqa_decode_step")
 
 
 def kv_cache_truncate(handle, seq_id, m):

@@ -63,10 +63,10 @@ gqa_status fail(gqa_status s, const std::string& msg) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 #ifndef GQA_DECODE_TARGET_BLOCKS
-#define GQA_DECODE_TARGET_BLOCKS 512
+#define GQA_DECODE_TARGET_BLOCKS 1024
 #endif
 #ifndef GQA_DECODE_MIN_PAGES
-#define GQA_DECODE_MIN_PAGES 8
+#define GQA_DECODE_MIN_PAGES 16
 #endif
 constexpr int kDecodeTargetBlocks = GQA_DECODE_TARGET_BLOCKS;   // workgroups a decode launch aims for
 constexpr int kDecodeMinPages = GQA_DECODE_MIN_PAGES;           // pages per split at least
@@ -506,23 +506,177 @@ GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, cons
 
 // ------------------------------------------------------------------ decode
 
+namespace {
+
 struct WsLayout {
-  int64_t max_splits, part_floats;
+  int64_t max_splits, part_floats, flags;
   size_t bytes;
 };
 
-// Workspace: split partials, [split][kv head][head chunk of <= 16][d + 4]
-// float32 records (o, then m and l).  Whatever the lengths, a call makes at
-// most ceil(target / (Hkv * chunks)) + B splits per (kv head, chunk).
+// Workspace: split records [split][kv head x head chunk][16][d + 4] float32
+// (o, then m and l), then int32 ready flags, one per (split, kv head x chunk).
+// Whatever the lengths, a call makes at most ceil(target / (Hkv * chunks)) + B
+// splits (see decode_splits).
 WsLayout ws_layout(const gqa_cache* c, int64_t B, int64_t Hq) {
   WsLayout w;
   const int64_t chunks = ceil_div(std::max<int64_t>(1, Hq / c->cfg.num_kv_heads), 16);
   const int64_t ys = c->cfg.num_kv_heads * chunks;
   w.max_splits = ceil_div(kDecodeTargetBlocks, ys) + B;
   w.part_floats = w.max_splits * ys * 16 * (static_cast<int64_t>(c->cfg.head_dim) + 4);
-  w.bytes = static_cast<size_t>(w.part_floats * 4);
+  w.flags = w.max_splits * ys;
+  w.bytes = static_cast<size_t>((w.part_floats + w.flags) * 4);
   return w;
 }
+
+// Pages per split: enough workgroups to fill the chip (about the target count),
+// at least kDecodeMinPages pages each, at most kMaxSplitDecode splits per
+// sequence (the in-kernel combine stages one weight per split in LDS).
+int decode_pages_per_split(const int32_t* T, int B, int64_t ys) {
+  int64_t total_pages = 0, max_pages = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t p = ceil_div(T[b], kPage);
+    total_pages += p;
+    max_pages = std::max(max_pages, p);
+  }
+  int64_t pps = std::max<int64_t>(kDecodeMinPages, ceil_div(total_pages * ys, kDecodeTargetBlocks));
+  pps = std::max<int64_t>(pps, ceil_div(max_pages, gqa::kMaxSplitDecode));
+  return static_cast<int>(pps);
+}
+
+// Launches decode attention for B sequences of lengths T[b] (query at T[b]-1).
+// With k_new/v_new (bf16 path) the same launch writes the token at T[b]-1.
+gqa_status launch_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
+                         const gqa_tensor* o, const int32_t* T, const gqa_tensor* k_new, const gqa_tensor* v_new,
+                         void* workspace, size_t ws_bytes, hipStream_t s) {
+  const gqa_cache_config& cf = c->cfg;
+  const int64_t Hq = q->shape[1];
+  const int G = static_cast<int>(Hq / cf.num_kv_heads);
+  const int hchunks = (G + 15) / 16;
+  const int64_t ys = static_cast<int64_t>(cf.num_kv_heads) * hchunks;
+  const int pps = decode_pages_per_split(T, B, ys);
+  int64_t total_splits = 0;
+  for (int b = 0; b < B; ++b) total_splits += ceil_div(ceil_div(T[b], kPage), pps);
+  float* part_o = nullptr;
+  int32_t* flags = nullptr;
+  if (total_splits > B) {
+    const WsLayout wl = ws_layout(c, B, Hq);
+    part_o = static_cast<float*>(workspace);
+    flags = reinterpret_cast<int32_t*>(part_o + wl.part_floats);
+  }
+  gqa_status st = sync_metadata(c, s);
+  if (st != GQA_OK) return st;
+  int64_t split_base = 0;
+  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+    gqa::DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
+    a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1];
+    a.o = static_cast<char*>(o->data) + b0 * o->stride[0] * c->elt;
+    a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1];
+    if (k_new) {
+      a.k_new = static_cast<const char*>(k_new->data) + b0 * k_new->stride[0] * c->elt;
+      a.kn_s0 = k_new->stride[0]; a.kn_s1 = k_new->stride[1];
+      a.v_new = static_cast<const char*>(v_new->data) + b0 * v_new->stride[0] * c->elt;
+      a.vn_s0 = v_new->stride[0]; a.vn_s1 = v_new->stride[1];
+    }
+    a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.table = c->d_table;
+    a.table_w = cf.max_pages_per_seq;
+    a.Hq = static_cast<int32_t>(Hq);
+    a.Hkv = cf.num_kv_heads;
+    a.d = cf.head_dim;
+    a.nseq = nb;
+    a.pages_per_split = pps;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
+    a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    a.part_o = part_o ? part_o + split_base * ys * 16 * (cf.head_dim + 4) : nullptr;
+    a.flags = flags ? flags + split_base * ys : nullptr;
+    int32_t off = 0;
+    for (int j = 0; j < nb; ++j) {
+      a.meta.seq[j] = seq_ids[b0 + j];
+      a.meta.start[j] = T[b0 + j] - 1;
+      a.meta.count[j] = 1;
+      a.meta.row0[j] = 0;
+      a.meta.total[j] = T[b0 + j];
+      a.split_off[j] = off;
+      off += static_cast<int>(ceil_div(ceil_div(T[b0 + j], kPage), pps));
+    }
+    a.split_off[nb] = off;
+    hipError_t e = gqa::launch_decode_bf16(a, off, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    split_base += off;
+  }
+  return GQA_OK;
+}
+
+gqa_status launch_decode_f32(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
+                             const gqa_tensor* o, const int32_t* T, hipStream_t s) {
+  const gqa_cache_config& cf = c->cfg;
+  gqa_status st = sync_metadata(c, s);
+  if (st != GQA_OK) return st;
+  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+    gqa::AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.Q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
+    a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1]; a.q_s2 = q->stride[2];
+    a.O = static_cast<char*>(o->data) + b0 * o->stride[0] * c->elt;
+    a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1]; a.o_s2 = o->stride[2];
+    a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
+    a.table = c->d_table;
+    a.table_w = cf.max_pages_per_seq;
+    a.Hq = static_cast<int32_t>(q->shape[1]);
+    a.Hkv = cf.num_kv_heads;
+    a.d = cf.head_dim;
+    a.n_rect = 1;
+    a.nseq = nb;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
+    a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    for (int j = 0; j < nb; ++j) {
+      a.meta.seq[j] = seq_ids[b0 + j];
+      a.meta.start[j] = T[b0 + j] - 1;
+      a.meta.count[j] = 1;
+      a.meta.row0[j] = 0;
+      a.meta.total[j] = T[b0 + j];
+    }
+    hipError_t e = gqa::launch_attend_f32(a, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  return GQA_OK;
+}
+
+// q/o checks shared by gqa_decode and gqa_decode_step; the workspace check
+// needs the lengths the call will attend over.
+gqa_status check_decode_args(const gqa_cache* c, int32_t B, const gqa_tensor* q, const gqa_tensor* o) {
+  const gqa_cache_config& cf = c->cfg;
+  if (!q || !o) return fail(GQA_ERR_ARG, "q or o is null");
+  const int64_t Hq = q->shape[1];
+  if (Hq < 1 || Hq % cf.num_kv_heads) return fail(GQA_ERR_SHAPE, "Hkv must divide Hq");
+  gqa_status st = check_tensor(q, "q", cf.dtype, B, Hq, 1, cf.head_dim);
+  if (st != GQA_OK) return st;
+  return check_tensor(o, "o", cf.dtype, B, Hq, 1, cf.head_dim);
+}
+
+gqa_status check_workspace(const gqa_cache* c, int32_t B, int64_t Hq, const int32_t* T, void* workspace,
+                           size_t ws_bytes) {
+  if (c->cfg.dtype != GQA_BF16 || B == 0) return GQA_OK;
+  const int G = static_cast<int>(Hq / c->cfg.num_kv_heads);
+  const int64_t ys = static_cast<int64_t>(c->cfg.num_kv_heads) * ((G + 15) / 16);
+  const int pps = decode_pages_per_split(T, B, ys);
+  int64_t total_splits = 0;
+  for (int b = 0; b < B; ++b) total_splits += ceil_div(ceil_div(T[b], kPage), pps);
+  if (total_splits <= B) return GQA_OK;
+  const WsLayout wl = ws_layout(c, B, Hq);
+  if (!workspace || ws_bytes < wl.bytes)
+    return fail(GQA_ERR_ARG, "workspace missing or smaller than gqa_workspace_size");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
+  return GQA_OK;
+}
+
+}  // namespace
 
 GQA_EXPORT size_t gqa_workspace_size(const gqa_cache* c, int32_t B, int32_t Hq) {
   if (!c || B < 0 || Hq < 1) return 0;
@@ -537,12 +691,7 @@ GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const i
   if (layer < 0 || layer >= cf.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
   gqa_status st = check_seqs(c, B, seq_ids);
   if (st != GQA_OK) return st;
-  if (!q || !o) return fail(GQA_ERR_ARG, "q or o is null");
-  const int64_t Hq = q->shape[1];
-  if (Hq < 1 || Hq % cf.num_kv_heads) return fail(GQA_ERR_SHAPE, "Hkv must divide Hq");
-  st = check_tensor(q, "q", cf.dtype, B, Hq, 1, cf.head_dim);
-  if (st != GQA_OK) return st;
-  st = check_tensor(o, "o", cf.dtype, B, Hq, 1, cf.head_dim);
+  st = check_decode_args(c, B, q, o);
   if (st != GQA_OK) return st;
   if (B > 0 && !valid_lengths) return fail(GQA_ERR_ARG, "valid_lengths is null");
   for (int b = 0; b < B; ++b) {
@@ -551,99 +700,46 @@ GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const i
     if (have < 1) return fail(GQA_ERR_CACHE, "decode needs at least one cached token");
   }
   if (B == 0) return GQA_OK;
-  const int G = static_cast<int>(Hq / cf.num_kv_heads);
-  const int hchunks = (G + 15) / 16;
-  int64_t total_pages = 0;
-  for (int b = 0; b < B; ++b) total_pages += ceil_div(valid_lengths[b], kPage);
-  const int64_t work = total_pages * cf.num_kv_heads * hchunks;
-  int64_t max_pages = 0;
-  for (int b = 0; b < B; ++b) max_pages = std::max<int64_t>(max_pages, ceil_div(valid_lengths[b], kPage));
-  // at most 128 splits per sequence (the merge kernel holds one weight per split in LDS)
-  const int pps = static_cast<int>(std::max<int64_t>(std::max<int64_t>(kDecodeMinPages, ceil_div(work, kDecodeTargetBlocks)),
-                                                     ceil_div(max_pages, 128)));
-  int64_t total_splits = 0;
-  for (int b = 0; b < B; ++b) total_splits += ceil_div(ceil_div(valid_lengths[b], kPage), pps);
-  const bool bf16 = cf.dtype == GQA_BF16;
-  float* part_o = nullptr;
-  if (bf16 && total_splits > B) {
-    const WsLayout wl = ws_layout(c, B, Hq);
-    if (!workspace || ws_bytes < wl.bytes)
-      return fail(GQA_ERR_ARG, "workspace missing or smaller than gqa_workspace_size");
-    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
-    part_o = static_cast<float*>(workspace);
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = sync_metadata(c, s);
+  st = check_workspace(c, B, q->shape[1], valid_lengths, workspace, ws_bytes);
   if (st != GQA_OK) return st;
-  int64_t split_base = 0;
-  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
-    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
-    const void* lk = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
-    const void* lv = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
-    if (!bf16) {
-      gqa::AttnArgs a;
-      std::memset(&a, 0, sizeof(a));
-      a.Q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
-      a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1]; a.q_s2 = q->stride[2];
-      a.O = static_cast<char*>(o->data) + b0 * o->stride[0] * c->elt;
-      a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1]; a.o_s2 = o->stride[2];
-      a.k_pool = lk;
-      a.v_pool = lv;
-      a.table = c->d_table;
-      a.table_w = cf.max_pages_per_seq;
-      a.Hq = static_cast<int32_t>(Hq);
-      a.Hkv = cf.num_kv_heads;
-      a.d = cf.head_dim;
-      a.n_rect = 1;
-      a.nseq = nb;
-      a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
-      a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
-      for (int j = 0; j < nb; ++j) {
-        a.meta.seq[j] = seq_ids[b0 + j];
-        a.meta.start[j] = valid_lengths[b0 + j] - 1;
-        a.meta.count[j] = 1;
-        a.meta.row0[j] = 0;
-        a.meta.total[j] = valid_lengths[b0 + j];
-      }
-      hipError_t e = gqa::launch_attend_f32(a, s);
-      if (e != hipSuccess) return hip_fail(e, "decode launch");
-      continue;
-    }
-    gqa::DecodeArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
-    a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1];
-    a.o = static_cast<char*>(o->data) + b0 * o->stride[0] * c->elt;
-    a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1];
-    a.k_pool = lk;
-    a.v_pool = lv;
-    a.table = c->d_table;
-    a.table_w = cf.max_pages_per_seq;
-    a.Hq = static_cast<int32_t>(Hq);
-    a.Hkv = cf.num_kv_heads;
-    a.d = cf.head_dim;
-    a.nseq = nb;
-    a.pages_per_split = pps;
-    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
-    a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
-    a.part_o = part_o ? part_o + split_base * cf.num_kv_heads * hchunks * 16 * (cf.head_dim + 4) : nullptr;
-    int32_t off = 0;
-    for (int j = 0; j < nb; ++j) {
-      const int T = valid_lengths[b0 + j];
-      a.meta.seq[j] = seq_ids[b0 + j];
-      a.meta.start[j] = T - 1;
-      a.meta.count[j] = 1;
-      a.meta.row0[j] = 0;
-      a.meta.total[j] = T;
-      a.split_off[j] = off;
-      off += static_cast<int>(ceil_div(ceil_div(T, kPage), pps));
-    }
-    a.split_off[nb] = off;
-    hipError_t e = gqa::launch_decode_bf16(a, off, off > nb, s);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-    split_base += off;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cf.dtype != GQA_BF16) return launch_decode_f32(c, layer, B, seq_ids, q, o, valid_lengths, s);
+  return launch_decode(c, layer, B, seq_ids, q, o, valid_lengths, nullptr, nullptr, workspace, ws_bytes, s);
+}
+
+GQA_EXPORT gqa_status gqa_decode_step(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
+                                      const gqa_tensor* q, const gqa_tensor* k_new, const gqa_tensor* v_new,
+                                      const gqa_tensor* o, void* workspace, size_t ws_bytes, void* stream) {
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const gqa_cache_config& cf = c->cfg;
+  if (layer < 0 || layer >= cf.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
+  gqa_status st = check_seqs(c, B, seq_ids);
+  if (st != GQA_OK) return st;
+  st = check_decode_args(c, B, q, o);
+  if (st != GQA_OK) return st;
+  if (B == 0) return GQA_OK;
+  // the new token sits at position c_b (the current length) of every sequence
+  std::vector<uint8_t> mask(B, 1);
+  std::vector<int32_t> pos(B);
+  for (int b = 0; b < B; ++b) pos[b] = c->len[static_cast<int64_t>(seq_ids[b]) * cf.num_layers + layer];
+  AppendPlan plan;
+  st = plan_append(c, layer, B, seq_ids, k_new, v_new, mask.data(), pos.data(), &plan);
+  if (st != GQA_OK) return st;
+  if (plan.n != 1) return fail(GQA_ERR_SHAPE, "k_new and v_new must hold one token: [B, Hkv, 1, d]");
+  std::vector<int32_t> T(B);
+  for (int b = 0; b < B; ++b) T[b] = pos[b] + 1;
+  st = check_workspace(c, B, q->shape[1], T.data(), workspace, ws_bytes);
+  if (st != GQA_OK) return st;
+  commit_append(c, layer, B, seq_ids, plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cf.dtype != GQA_BF16) {
+    st = sync_metadata(c, s);
+    if (st != GQA_OK) return st;
+    st = launch_append_all(c, layer, B, seq_ids, k_new, v_new, plan, s);
+    if (st != GQA_OK) return st;
+    return launch_decode_f32(c, layer, B, seq_ids, q, o, T.data(), s);
   }
-  return GQA_OK;
+  return launch_decode(c, layer, B, seq_ids, q, o, T.data(), k_new, v_new, workspace, ws_bytes, s);
 }
 
 // ------------------------------------------------------------------ truncate / remap

@@ -10,6 +10,7 @@ namespace gqa {
 constexpr int kPage = 16;          // tokens per page
 constexpr int kMaxSeqPerLaunch = 64;
 constexpr int kMaxPatchPerLaunch = 240;
+constexpr int kMaxSplitDecode = 128;   // splits per sequence in one decode launch
 
 // Per-sequence metadata of one launch.
 //  start: position of the first valid token of the call (= cache length before
@@ -68,15 +69,20 @@ struct DecodeArgs {
   int64_t q_s0, q_s1;
   void* o;
   int64_t o_s0, o_s1;
-  const void* k_pool;
-  const void* v_pool;
+  const void* k_new;          // optional new token appended by the same launch: [B][Hkv][1][d]
+  int64_t kn_s0, kn_s1;
+  const void* v_new;
+  int64_t vn_s0, vn_s1;
+  void* k_pool;               // this layer's pool base (written only for the new token)
+  void* v_pool;
   const int32_t* table;
   int32_t table_w;
   int32_t Hq, Hkv, d, nseq;
   int32_t pages_per_split;
   float scale_log2;
   const float* rope;
-  float* part_o;              // split partials: [split][y][16][d + 4] (o, m, l)
+  float* part_o;              // split records: [split][y][16][d + 4] (o, m, l)
+  int32_t* flags;             // ready flags, one per split record group; zero between calls
   int32_t split_off[kMaxSeqPerLaunch + 1];
   SeqMeta meta;               // start = T-1, total = T
 };
@@ -97,7 +103,7 @@ hipError_t launch_table_patch(const PatchArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int grid_x, hipStream_t s);
 hipError_t launch_attend_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, bool merge, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s);
 hipError_t launch_page_copy(const CopyArgs& a, int num_layers, hipStream_t s);
 
 }  // namespace gqa

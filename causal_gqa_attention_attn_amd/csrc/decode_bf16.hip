@@ -1,42 +1,67 @@
-// bfloat16 split-T decode attention over the paged cache.
+// bfloat16 split-T decode attention over the paged cache, one launch per layer.
 //
 // What it computes (page "模型执行：从 token 到 Prefill 与 Decode", prefill and
 // decode shapes; page "KV Cache 与 Prefill/Decode 推理路径", single-token
 // decode needs no mask): one new query per sequence, at position T-1, attends
 // to all T cached slots of its KV head g(h) = floor(h*Hkv/Hq):
 //   o[b,h] = sum_{j<T} softmax_j(<rot(q), k_used[g,j]>/sqrt(d)) v[g,j].
+// Optionally the same launch first appends the step's new token (slot T-1):
+// its key is rotated with the query's rotation row (same position) and
+// rounded to bf16, its value copied, both written to the cache and used
+// straight from registers.
 //
 // How (memory-bound; every K/V byte is read from HBM once per step):
 //  * one workgroup = (sequence, split of consecutive pages, kv head, up to 16
-//    query heads of its group); its four waves take the split's pages in turn;
+//    query heads of its group); its four waves take the split's pages in turn,
+//    each with up to four pages in flight; the block-table entries, the query
+//    and its rotation row are requested together before any is used;
 //  * per page: S^T[16 keys x 16 heads] = K q^T on v_mfma_f32_16x16x32_bf16 with
-//    the K rows loaded straight from the page (16-byte loads, the whole page is
-//    one contiguous 4 KiB run for d=128), then O^T[d x heads] += V^T P^T on
-//    v_mfma_f32_16x16x16_bf16 with V^T read straight from the d-major page;
+//    the K rows loaded straight from the page, then O^T[d x heads] += V^T P^T
+//    on v_mfma_f32_16x16x16_bf16 with V^T read straight from the d-major page;
 //    the score accumulator is already the B operand of the second product;
-//  * online softmax in base 2 per head; the four waves and then the splits
-//    are combined with the log-sum-exp rule: with M = max_s m_s,
+//  * online softmax in base 2 per head; the four waves, then the splits, are
+//    combined with the log-sum-exp rule: with M = max_s m_s,
 //    O = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);
-//  * a sequence whose pages fit one split writes its output directly; the
-//    others write (m, l, o) partials that decode_merge_kernel, launched next on
-//    the same stream, combines (the kernel boundary makes the partials visible;
-//    no cross-workgroup atomics: same-address device-scope atomics serialise
-//    across the chip's XCDs).
+//  * split combine inside the launch, without atomics (same-address
+//    device-scope atomics serialise across the chip's XCDs): every split but the
+//    last writes its (m, l, o) record and then a ready flag with device-scope
+//    stores; the last split of the (sequence, kv head) - the highest workgroup
+//    index of its group, so it only waits on workgroups dispatched before it -
+//    polls those flags with a bounded spin, combines, writes the output and
+//    clears the flags for the next call.
 #include "common.hpp"
 #include "device.hpp"
 
 namespace gqa {
 
+namespace {
+
+constexpr int kSpinLimit = 1 << 18;        // bounded wait for a split's flag
+
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NQ = D / 32;      // k-steps of the score product
   constexpr int NDB = D / 16;     // 16-row blocks of the output
+  constexpr int kRec = D + 4;     // partial record: o[D], m, l, pad
   __shared__ float red_m[4][16];
   __shared__ float red_l[4][16];
   __shared__ float red_o[4][16][D + 4];
+  __shared__ float s_w[16][kMaxSplitDecode];
+  __shared__ float s_M[16];
+  __shared__ int s_ok;
 
   const int G = a.Hq / a.Hkv;
   const int hchunks = (G + 15) >> 4;
+  const int gy = gridDim.y;
   const int g = blockIdx.y / hchunks;
   const int hcb = blockIdx.y - g * hchunks;
   int b = 0;
@@ -56,32 +81,95 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int c16 = lane & 15;
   const int hl = hcb * 16 + c16;           // head within the group held by this lane column
   const bool hvalid = hl < G;
-  const int h = g * G + hl;
+  const int Gc = min(16, G - hcb * 16);
 
-  // rotated query as B operand: lane (head c16, grp) holds dims 32c + 8*grp + 0..7
-  bf16x8 qf[NQ];
-  {
-    float x[NQ][8];
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.q_s0 + static_cast<int64_t>(h) * a.q_s1;
+  uint16_t* kpool = static_cast<uint16_t*>(a.k_pool);
+  uint16_t* vpool = static_cast<uint16_t*>(a.v_pool);
+  const int32_t* trow = a.table + static_cast<int64_t>(seq) * a.table_w;
+  const int Hkv = a.Hkv;
+  const float sl2 = a.scale_log2;
+
+  // the step's new token (slot T-1) lives in the last page, so in the last split
+  const bool owns_new = a.k_new != nullptr && split == nsplit - 1;
+  const int p_new = (T - 1) >> 4;
+  const int r_new = (T - 1) & 15;
+
+  // Everything the first batch needs is requested before anything is used:
+  // the block-table entries of this wave's pages, the query, its rotation row
+  // and the new token.  Loads are unconditional (indices clamped to valid
+  // rows) so the compiler issues them back to back.
+  constexpr int kBatch = 4;
+  const int p_first = p_begin + wave;
+  int64_t phys[kBatch];
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (hvalid) w = *reinterpret_cast<const u32x4*>(qrow + c * 32 + grp * 8);
+  for (int j = 0; j < kBatch; ++j) phys[j] = trow[min(p_first + 4 * j, p_end - 1)];
+  const int hq = g * G + min(hl, G - 1);
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.q_s0 + static_cast<int64_t>(hq) * a.q_s1;
+  u32x4 qw[NQ];
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) qw[c] = *reinterpret_cast<const u32x4*>(qrow + c * 32 + grp * 8);
+  u32x4 kw[NQ];
+  uint32_t vw[NDB];
+  if (owns_new) {
+    const uint16_t* krow = static_cast<const uint16_t*>(a.k_new) + b * a.kn_s0 + static_cast<int64_t>(g) * a.kn_s1;
+    const uint16_t* vrow = static_cast<const uint16_t*>(a.v_new) + b * a.vn_s0 + static_cast<int64_t>(g) * a.vn_s1;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) kw[c] = *reinterpret_cast<const u32x4*>(krow + c * 32 + grp * 8);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vw[db] = vrow[db * 16 + c16];
+  }
+  float cs[NQ / 2][8][2];
+  if (a.rope) {
+    const float* rrow = a.rope + static_cast<int64_t>(qpos) * D;
+#pragma unroll
+    for (int c = 0; c < NQ / 2; ++c) {
+      const float4* r4 = reinterpret_cast<const float4*>(rrow + 2 * (c * 32 + grp * 8));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[c][2 * e] = __uint_as_float(w[e] << 16);
-        x[c][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        const float4 v = r4[e];
+        cs[c][2 * e][0] = v.x;
+        cs[c][2 * e][1] = v.y;
+        cs[c][2 * e + 1][0] = v.z;
+        cs[c][2 * e + 1][1] = v.w;
       }
     }
-    if (a.rope && hvalid) {
-      const float* rrow = a.rope + static_cast<int64_t>(qpos) * D;
+  }
+  auto load_pages = [&](const int64_t* ph, bf16x8 (*kf)[NQ], u32x2 (*vf)[NDB]) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const uint16_t* kpage = kpool + (ph[j] * Hkv + g) * (kPage * D);
+      const uint16_t* vpage = vpool + (ph[j] * Hkv + g) * (D * kPage);
+#pragma unroll
+      for (int c = 0; c < NQ; ++c)
+        kf[j][c] = *reinterpret_cast<const bf16x8*>(kpage + c16 * D + c * 32 + grp * 8);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        vf[j][db] = *reinterpret_cast<const u32x2*>(vpage + (db * 16 + c16) * kPage + grp * 4);
+    }
+  };
+  bf16x8 kf[kBatch][NQ];
+  u32x2 vf[kBatch][NDB];
+  load_pages(phys, kf, vf);
+
+  // rotate (pairs i, i + D/2) and round to bf16: the query, and the new key
+  // with the same rotation row
+  auto rotate_round = [&](const u32x4* w_in, bool valid, bf16x8* out) {
+    float x[NQ][8];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = valid ? w_in[c][e] : 0u;
+        x[c][2 * e] = __uint_as_float(w << 16);
+        x[c][2 * e + 1] = __uint_as_float(w & 0xffff0000u);
+      }
+    if (a.rope) {
 #pragma unroll
       for (int c = 0; c < NQ / 2; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int i = c * 32 + grp * 8 + e;
           float lo, hi;
-          rotate_pair(x[c][e], x[c + NQ / 2][e], rrow[2 * i], rrow[2 * i + 1], lo, hi);
+          rotate_pair(x[c][e], x[c + NQ / 2][e], cs[c][e][0], cs[c][e][1], lo, hi);
           x[c][e] = lo;
           x[c + NQ / 2][e] = hi;
         }
@@ -91,15 +179,30 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[c][2 * e], x[c][2 * e + 1]);
-      qf[c] = __builtin_bit_cast(bf16x8, w);
+      out[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  bf16x8 qf[NQ];
+  rotate_round(qw, hvalid, qf);
+  bf16x8 knew[NQ];
+  if (owns_new) {
+    rotate_round(kw, true, knew);
+    // write the new token to the cache: the wave whose page it is, key row by
+    // the lanes of row r_new, value column by the lanes of its 4-slot group
+    if (p_new >= p_begin && ((p_new - p_begin) & 3) == wave) {
+      const int64_t ph = trow[p_new];
+      if (c16 == r_new) {
+        uint16_t* kdst = kpool + ((ph * Hkv + g) * kPage + r_new) * D;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) *reinterpret_cast<bf16x8*>(kdst + c * 32 + grp * 8) = knew[c];
+      }
+      if (grp == (r_new >> 2)) {
+        uint16_t* vdst = vpool + (ph * Hkv + g) * (D * kPage) + r_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vdst[(db * 16 + c16) * kPage] = static_cast<uint16_t>(vw[db]);
+      }
     }
   }
-
-  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
-  const int32_t* trow = a.table + static_cast<int64_t>(seq) * a.table_w;
-  const int Hkv = a.Hkv;
-  const float sl2 = a.scale_log2;
 
   f32x4 o[NDB];
 #pragma unroll
@@ -107,31 +210,33 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   float m_run = -1e30f;
   float l_run = 0.f;
 
-  // wave w takes pages p_begin + w, + 4, ...; up to kBatch of them are loaded
-  // before any is used so that many 4 KiB page reads are in flight per wave
-  constexpr int kBatch = 4;
-  for (int p0 = p_begin + wave; p0 < p_end; p0 += 4 * kBatch) {
-    bf16x8 kf[kBatch][NQ];
-    u32x2 vf[kBatch][NDB];
+  // wave w takes pages p_begin + w, + 4, ...; kBatch of them are in flight at
+  // a time (pages past the split's end reload its last page and are skipped)
+  for (int p0 = p_first; p0 < p_end; p0 += 4 * kBatch) {
+    if (p0 != p_first) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      // pages past the split's end reload its last page (no extra HBM traffic,
-      // no branch between the loads) and are skipped below
-      const int p = min(p0 + 4 * j, p_end - 1);
-      const int64_t phys = trow[p];
-      const uint16_t* kpage = kpool + (phys * Hkv + g) * (kPage * D);
-      const uint16_t* vpage = vpool + (phys * Hkv + g) * (D * kPage);
-#pragma unroll
-      for (int c = 0; c < NQ; ++c)
-        kf[j][c] = *reinterpret_cast<const bf16x8*>(kpage + c16 * D + c * 32 + grp * 8);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        vf[j][db] = *reinterpret_cast<const u32x2*>(vpage + (db * 16 + c16) * kPage + grp * 4);
+      for (int j = 0; j < kBatch; ++j) phys[j] = trow[min(p0 + 4 * j, p_end - 1)];
+      load_pages(phys, kf, vf);
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int p = p0 + 4 * j;
       if (p >= p_end) break;
+      if (owns_new && p == p_new) {
+        // slot T-1 from registers: whatever the page held there is ignored
+        if (c16 == r_new) {
+#pragma unroll
+          for (int c = 0; c < NQ; ++c) kf[j][c] = knew[c];
+        }
+        if (grp == (r_new >> 2)) {
+          const int e = r_new & 3;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const uint32_t word = vf[j][db][e >> 1];
+            vf[j][db][e >> 1] = (e & 1) ? ((word & 0x0000ffffu) | (vw[db] << 16)) : ((word & 0xffff0000u) | vw[db]);
+          }
+        }
+      }
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NQ; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][c], qf[c], s, 0, 0, 0);
@@ -187,117 +292,119 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   // 256 threads: head column hh = tid / 16, 16 threads per head over d
   const int hh = threadIdx.x >> 4;
   const int dl = threadIdx.x & 15;
-  const int hl2 = hcb * 16 + hh;
-  const bool hv2 = hl2 < G;
-  const int h2 = g * G + hl2;
+  const bool hv2 = hh < Gc;
+  const int h2 = g * G + hcb * 16 + hh;
   float M = red_m[0][hh];
 #pragma unroll
   for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
-  float sc[4];
   float L = 0.f;
+  float acc[D / 16];
+  {
+    float sc[4];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    sc[w] = __builtin_amdgcn_exp2f(red_m[w][hh] - M);
-    L += red_l[w][hh] * sc[w];
+    for (int w = 0; w < 4; ++w) {
+      sc[w] = __builtin_amdgcn_exp2f(red_m[w][hh] - M);
+      L += red_l[w][hh] * sc[w];
+    }
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += red_o[w][hh][dl + 16 * k] * sc[w];
+      acc[k] = v;
+    }
   }
   uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(h2) * a.o_s1;
   if (nsplit == 1) {
     if (!hv2) return;
     const float inv = 1.f / L;
-    for (int dd = dl; dd < D; dd += 16) {
-      float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc += red_o[w][hh][dd] * sc[w];
-      orow[dd] = f32_to_bf16(acc * inv);
-    }
+    for (int k = 0; k < D / 16; ++k) orow[dl + 16 * k] = f32_to_bf16(acc[k] * inv);
     return;
   }
 
-  // several splits: write this split's (m, l, o); decode_merge_kernel, the
-  // next launch on the stream, combines them.  Partials of one (sequence,
-  // blockIdx.y) are contiguous: [split][head in chunk][D + 4] floats, o in
-  // 0..D-1 and (m, l) at D, D+1.
-  if (!hv2) return;
-  constexpr int kRec = D + 4;
-  const int Gc = min(16, G - hcb * 16);
-  float* rec = a.part_o + ((static_cast<int64_t>(a.split_off[b]) * gridDim.y +
-                            static_cast<int64_t>(blockIdx.y) * nsplit) * 16 +
-                           static_cast<int64_t>(split) * Gc + hh) * kRec;
-  for (int dd = dl; dd < D; dd += 16) {
-    float acc = 0.f;
+  // partial records of this (sequence, blockIdx.y): [split][head in chunk][kRec]
+  const int64_t group = static_cast<int64_t>(a.split_off[b]) * gy + static_cast<int64_t>(blockIdx.y) * nsplit;
+  float* region = a.part_o + group * (16 * kRec);
+  int32_t* flags = a.flags + group;
+  if (split != nsplit - 1) {
+    if (hv2) {
+      float* rec = region + (static_cast<int64_t>(split) * Gc + hh) * kRec;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc += red_o[w][hh][dd] * sc[w];
-    rec[dd] = acc;
+      for (int k = 0; k < D / 16; ++k) store_dev(rec + dl + 16 * k, acc[k]);
+      if (dl == 0) {
+        store_dev(rec + D, M);
+        store_dev(rec + D + 1, L);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);      // this thread's record has reached the device
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flags + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
-  if (dl == 0) {
-    rec[D] = M;
-    rec[D + 1] = L;
+
+  // the last split: wait for the others (bounded), then combine
+  const int others = nsplit - 1;
+  if (threadIdx.x == 0) s_ok = 1;
+  __syncthreads();
+  for (int t = threadIdx.x; t < others; t += 256) {
+    int spins = 0;
+    while (__hip_atomic_load(flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && spins < kSpinLimit) {
+      __builtin_amdgcn_s_sleep(2);
+      ++spins;
+    }
+    if (spins >= kSpinLimit) s_ok = 0;
   }
+  __syncthreads();
+  // maxima of every split (its own included) and their weights
+  for (int r = threadIdx.x; r < others * Gc; r += 256) {
+    const int sp = r / Gc;
+    const int hl3 = r - sp * Gc;
+    s_w[hl3][sp] = load_dev(region + static_cast<int64_t>(r) * kRec + D);
+  }
+  if (dl == 0 && hv2) s_w[hh][others] = M;
+  __syncthreads();
+  if (threadIdx.x < Gc) {
+    float mm = -INFINITY;
+    for (int sp = 0; sp <= others; ++sp) mm = fmaxf(mm, s_w[threadIdx.x][sp]);
+    s_M[threadIdx.x] = mm;
+  }
+  __syncthreads();
+  if (hv2) {
+    const float Mg = s_M[hh];
+    const float wown = __builtin_amdgcn_exp2f(M - Mg);
+    float Lg = L * wown;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) acc[k] *= wown;
+    for (int s0 = 0; s0 < others; s0 += 8) {
+      float v[8][D / 16 + 1];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* rec = region + (static_cast<int64_t>(min(s0 + u, others - 1)) * Gc + hh) * kRec;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) v[u][k] = load_dev(rec + dl + 16 * k);
+        v[u][D / 16] = load_dev(rec + D + 1);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u < others) {
+          const float w = __builtin_amdgcn_exp2f(s_w[hh][s0 + u] - Mg);
+#pragma unroll
+          for (int k = 0; k < D / 16; ++k) acc[k] += v[u][k] * w;
+          Lg += v[u][D / 16] * w;
+        }
+      }
+    }
+    const float inv = s_ok ? 1.f / Lg : __builtin_nanf("");
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) orow[dl + 16 * k] = f32_to_bf16(acc[k] * inv);
+  }
+  // leave every flag of the group at zero for the next call
+  for (int t = threadIdx.x; t < others; t += 256)
+    __hip_atomic_store(flags + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// grid: x = sequence, y = query head; one thread per output dimension.
-// Combines the split partials of sequences that needed more than one split:
-// with M = max_s m_s, o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-template <int D>
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int kRec = D + 4;
-  constexpr int kMaxSplit = 128;
-  const int b = blockIdx.x;
-  const int h = blockIdx.y;
-  const int nsplit = a.split_off[b + 1] - a.split_off[b];
-  if (nsplit <= 1) return;
-  const int G = a.Hq / a.Hkv;
-  const int hchunks = (G + 15) >> 4;
-  const int gy = a.Hkv * hchunks;
-  const int g = h / G;
-  const int hl = h - g * G;
-  const int hcb = hl >> 4;
-  const int hh = hl & 15;
-  const int Gc = min(16, G - hcb * 16);
-  const int y = g * hchunks + hcb;
-  const float* region = a.part_o + (static_cast<int64_t>(a.split_off[b]) * gy + static_cast<int64_t>(y) * nsplit) *
-                                       (16 * kRec);
-  __shared__ float s_w[kMaxSplit];
-  __shared__ float s_red[2][4];
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wv = t >> 6;
-  float m = -INFINITY, l = 0.f;
-  if (t < nsplit) {
-    const float* r = region + (static_cast<int64_t>(t) * Gc + hh) * kRec;
-    m = r[D];
-    l = r[D + 1];
-  }
-  float M = m;
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if (lane == 0) s_red[0][wv] = M;
-  __syncthreads();
-  M = fmaxf(s_red[0][0], s_red[0][1]);
-  const float w = t < nsplit ? __builtin_amdgcn_exp2f(m - M) : 0.f;
-  if (t < nsplit) s_w[t] = w;
-  float L = l * w;
-  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-  if (lane == 0) s_red[1][wv] = L;
-  __syncthreads();
-  L = s_red[1][0] + s_red[1][1];
-  if (t >= D) return;
-  const float* col = region + static_cast<int64_t>(hh) * kRec + t;
-  const int64_t stride = static_cast<int64_t>(Gc) * kRec;
-  float acc = 0.f;
-  int sp = 0;
-  for (; sp + 16 <= nsplit; sp += 16) {
-    float v[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = col[(sp + k) * stride];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) acc += v[k] * s_w[sp + k];
-  }
-  for (; sp < nsplit; ++sp) acc += col[sp * stride] * s_w[sp];
-  uint16_t* out = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(h) * a.o_s1;
-  out[t] = f32_to_bf16(acc / L);
-}
-
-hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, bool merge, hipStream_t s) {
+hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int hchunks = (G + 15) / 16;
   dim3 grid(total_splits, a.Hkv * hchunks);
@@ -305,12 +412,6 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, bool merge,
     hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !merge) return e;
-  if (a.d == 128)
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.nseq, a.Hq), dim3(128), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.nseq, a.Hq), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

@@ -164,13 +164,25 @@ gqa_status gqa_attention(gqa_cache* cache, int32_t layer, int32_t B, const int32
  * one query per sequence at position T_b - 1 against all T_b cached slots of
  * layer `layer`.  valid_lengths (host int32 [B]) must equal each sequence's
  * current length in that layer (append the new token's K/V first) and be >= 1.
- * q and o are [B,Hq,1,d].  workspace: device scratch for split partials, at
- * least gqa_workspace_size(cache, B, Hq) bytes, 256-byte aligned; calls that
- * share a workspace must not overlap in time.  It may be NULL when every
- * sequence fits one split (short caches). */
+ * q and o are [B,Hq,1,d].  workspace: device scratch for split partials and
+ * ready flags, at least gqa_workspace_size(cache, B, Hq) bytes, 256-byte
+ * aligned and ZERO-FILLED before its first use (every call leaves its flags at
+ * zero again, so one zeroed workspace serves any number of ordered calls).
+ * Calls that share a workspace must not overlap in time.  It may be NULL when
+ * every sequence fits one split (short caches). */
 gqa_status gqa_decode(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
                       const gqa_tensor* q, const int32_t* valid_lengths, const gqa_tensor* o,
                       void* workspace, size_t ws_bytes, void* stream);
+
+/* One decode step in one launch: kv_cache_append of the new token (k_new,
+ * v_new [B,Hkv,1,d], position = the layer's current length c_b, rotated with
+ * that position) followed by gqa_decode with T_b = c_b + 1 ([P3] decode
+ * lessons: each step appends one K/V per layer, then the new query reads all T
+ * entries).  Same results, cache contents and page assignment as the two calls;
+ * bf16 caches do both in a single kernel.  Same workspace rule as gqa_decode. */
+gqa_status gqa_decode_step(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
+                           const gqa_tensor* q, const gqa_tensor* k_new, const gqa_tensor* v_new,
+                           const gqa_tensor* o, void* workspace, size_t ws_bytes, void* stream);
 
 /* Prompt edit at position m ([P3] prompt-edit lesson): keep positions [0,m) in
  * every layer of seq_id, drop the rest and return pages no layer still uses to
@@ -197,9 +209,9 @@ gqa_status gqa_cache_free_pages(const gqa_cache* cache, int32_t* out);
  * page is either free or owned by exactly one sequence.  GQA_ERR_CACHE if not. */
 gqa_status gqa_cache_check(const gqa_cache* cache);
 
-/* Device workspace bytes that suffice for gqa_decode with up to B sequences and
- * Hq query heads, whatever their lengths.  gqa_prefill and gqa_attention need
- * none. */
+/* Device workspace bytes that suffice for gqa_decode / gqa_decode_step with up
+ * to B sequences and Hq query heads, whatever their lengths (zero-fill it once
+ * before first use).  gqa_prefill and gqa_attention need none. */
 size_t gqa_workspace_size(const gqa_cache* cache, int32_t B, int32_t Hq);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -82,6 +82,20 @@ class Pair:
         self.append(layer, seq_ids, st.k, st.v, mask, pos)
         return self.decode(layer, seq_ids, st.q, [n + 1 for n in lens])
 
+    def step_fused(self, layer, seq_ids, st):
+        """One decode step through gqa_decode_step (append + decode in one call)."""
+        lens = [self.ref.cache_length(s, layer) for s in seq_ids]
+        qd = st.q.to("cuda")
+        o = torch.full_like(qd, float("nan"))
+        self.lib.gqa_decode_step(self.gpu.handle, layer, seq_ids, qd, st.k.to("cuda"), st.v.to("cuda"), o,
+                                 self.workspace(len(seq_ids), st.q.shape[1]))
+        torch.cuda.synchronize()
+        B = len(seq_ids)
+        self.ref.append(layer, seq_ids, as_f32(st.k), as_f32(st.v), np.ones((B, 1), np.uint8),
+                        np.array([[n] for n in lens]))
+        ref = self.ref.decode(layer, seq_ids, as_f32(st.q), [n + 1 for n in lens])
+        return o, ref
+
     def truncate(self, seq, m):
         self.lib.kv_cache_truncate(self.gpu.handle, seq, m)
         self.ref.truncate(seq, m)

@@ -408,8 +408,11 @@ def test_decode_graph_replay_matches_eager():
 
     def run():
         for l in range(L):
-            lib.kv_cache_append(c.handle, l, [0], k[l], v[l], one, pn)
-            lib.gqa_decode(c.handle, l, [0], q[l], [N], o[l], ws)
+            if l % 2:
+                lib.gqa_decode_step(c.handle, l, [0], q[l], k[l], v[l], o[l], ws)
+            else:
+                lib.kv_cache_append(c.handle, l, [0], k[l], v[l], one, pn)
+                lib.gqa_decode(c.handle, l, [0], q[l], [N], o[l], ws)
 
     run()
     torch.cuda.synchronize()
@@ -446,3 +449,30 @@ def test_prefill_second_pass_on_score_overflow():
     compare_rows(O, ref, torch.bfloat16)
     # rows after the spike are dominated by it: their output is value row 150
     assert torch.allclose(O[0, 0, 160].float().cpu(), inp.V[0, 0, 150].float(), atol=1e-2)
+
+
+@pytest.mark.parametrize("Hq,Hkv,lengths", [(48, 8, [700]), (32, 8, [33, 320, 1]), (32, 1, [257, 90]),
+                                            (8, 2, [16, 47])])
+def test_decode_step_fused(Hq, Hkv, lengths):
+    say(f"case: gqa_decode_step (append + decode in one launch) Hq={Hq} Hkv={Hkv} lengths={lengths}")
+    B = len(lengths)
+    d = 128
+    shape = W.AttnShape(B=B, n=max(lengths), Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4)
+    inp = W.prefill_inputs(shape, 71 + Hq, lengths=lengths)
+    a = Pair(1, Hkv, d, 256, B, 64, torch.bfloat16, 1e4, free_order=W.page_order(256, 8))
+    b = Pair(1, Hkv, d, 256, B, 64, torch.bfloat16, 1e4, free_order=W.page_order(256, 8))
+    ids = list(range(B))
+    for p in (a, b):
+        p.append(0, ids, inp.K, inp.V, inp.mask, inp.positions)
+    for t in range(3):
+        st = W.decode_step_inputs(shape, 71, t)
+        o1, r1 = a.step_fused(0, ids, st)
+        o2, _ = b.step(0, ids, st)
+        compare_rows(o1, r1, torch.bfloat16)
+        assert torch.equal(o1.cpu().view(torch.int16), o2.cpu().view(torch.int16)), f"step {t}"
+    a.check_cache(ids)
+    for s in ids:
+        ka, va = a.gpu.gather(s, 0)
+        kb, vb = b.gpu.gather(s, 0)
+        assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
+        assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
