@@ -509,12 +509,13 @@ GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, cons
 namespace {
 
 struct WsLayout {
-  int64_t max_splits, part_floats, flags;
+  int64_t max_splits, part_floats, hdr_floats, flags;
   size_t bytes;
 };
 
-// Workspace: split records [split][kv head x head chunk][16][d + 4] float32
-// (o, then m and l), then int32 ready flags, one per (split, kv head x chunk).
+// Workspace: split o rows [split][kv head x head chunk][16][d] float32, then
+// (m, l) headers [split][kv head x head chunk][16][2] float32, then int32 ready
+// flags, kDecodeMergers per (split, kv head x chunk).
 // Whatever the lengths, a call makes at most ceil(target / (Hkv * chunks)) + B
 // splits (see decode_splits).
 WsLayout ws_layout(const gqa_cache* c, int64_t B, int64_t Hq) {
@@ -522,9 +523,10 @@ WsLayout ws_layout(const gqa_cache* c, int64_t B, int64_t Hq) {
   const int64_t chunks = ceil_div(std::max<int64_t>(1, Hq / c->cfg.num_kv_heads), 16);
   const int64_t ys = c->cfg.num_kv_heads * chunks;
   w.max_splits = ceil_div(kDecodeTargetBlocks, ys) + B;
-  w.part_floats = w.max_splits * ys * 16 * (static_cast<int64_t>(c->cfg.head_dim) + 4);
-  w.flags = w.max_splits * ys;
-  w.bytes = static_cast<size_t>((w.part_floats + w.flags) * 4);
+  w.part_floats = w.max_splits * ys * 16 * static_cast<int64_t>(c->cfg.head_dim);
+  w.hdr_floats = w.max_splits * ys * 16 * 2;
+  w.flags = w.max_splits * ys * gqa::kDecodeMergers;
+  w.bytes = static_cast<size_t>((w.part_floats + w.hdr_floats + w.flags) * 4);
   return w;
 }
 
@@ -557,11 +559,13 @@ gqa_status launch_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* 
   int64_t total_splits = 0;
   for (int b = 0; b < B; ++b) total_splits += ceil_div(ceil_div(T[b], kPage), pps);
   float* part_o = nullptr;
+  float* part_h = nullptr;
   int32_t* flags = nullptr;
   if (total_splits > B) {
     const WsLayout wl = ws_layout(c, B, Hq);
     part_o = static_cast<float*>(workspace);
-    flags = reinterpret_cast<int32_t*>(part_o + wl.part_floats);
+    part_h = part_o + wl.part_floats;
+    flags = reinterpret_cast<int32_t*>(part_h + wl.hdr_floats);
   }
   gqa_status st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
@@ -591,8 +595,9 @@ gqa_status launch_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* 
     a.pages_per_split = pps;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
-    a.part_o = part_o ? part_o + split_base * ys * 16 * (cf.head_dim + 4) : nullptr;
-    a.flags = flags ? flags + split_base * ys : nullptr;
+    a.part_o = part_o ? part_o + split_base * ys * 16 * cf.head_dim : nullptr;
+    a.part_h = part_h ? part_h + split_base * ys * 16 * 2 : nullptr;
+    a.flags = flags ? flags + split_base * ys * gqa::kDecodeMergers : nullptr;
     int32_t off = 0;
     for (int j = 0; j < nb; ++j) {
       a.meta.seq[j] = seq_ids[b0 + j];

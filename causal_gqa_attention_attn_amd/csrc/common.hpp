@@ -11,6 +11,7 @@ constexpr int kPage = 16;          // tokens per page
 constexpr int kMaxSeqPerLaunch = 64;
 constexpr int kMaxPatchPerLaunch = 240;
 constexpr int kMaxSplitDecode = 128;   // splits per sequence in one decode launch
+constexpr int kDecodeMergers = 4;      // splits of a sequence that combine the split records
 
 // Per-sequence metadata of one launch.
 //  start: position of the first valid token of the call (= cache length before
@@ -81,8 +82,9 @@ struct DecodeArgs {
   int32_t pages_per_split;
   float scale_log2;
   const float* rope;
-  float* part_o;              // split records: [split][y][16][d + 4] (o, m, l)
-  int32_t* flags;             // ready flags, one per split record group; zero between calls
+  float* part_o;              // split o rows [split][y][16][d]
+  float* part_h;              // split (m, l) headers [split][y][16][2]
+  int32_t* flags;             // ready flags [split group][merger][split]; zero between calls
   int32_t split_off[kMaxSeqPerLaunch + 1];
   SeqMeta meta;               // start = T-1, total = T
 };

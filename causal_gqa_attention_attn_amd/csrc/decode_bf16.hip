@@ -13,7 +13,7 @@
 // How (memory-bound; every K/V byte is read from HBM once per step):
 //  * one workgroup = (sequence, split of consecutive pages, kv head, up to 16
 //    query heads of its group); its four waves take the split's pages in turn,
-//    each with up to four pages in flight; the block-table entries, the query
+//    each with two pages in flight; the block-table entries, the query
 //    and its rotation row are requested together before any is used;
 //  * per page: S^T[16 keys x 16 heads] = K q^T on v_mfma_f32_16x16x32_bf16 with
 //    the K rows loaded straight from the page, then O^T[d x heads] += V^T P^T
@@ -23,12 +23,14 @@
 //    combined with the log-sum-exp rule: with M = max_s m_s,
 //    O = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);
 //  * split combine inside the launch, without atomics (same-address
-//    device-scope atomics serialise across the chip's XCDs): every split but the
-//    last writes its (m, l, o) record and then a ready flag with device-scope
-//    stores; the last split of the (sequence, kv head) - the highest workgroup
-//    index of its group, so it only waits on workgroups dispatched before it -
-//    polls those flags with a bounded spin, combines, writes the output and
-//    clears the flags for the next call.
+//    device-scope atomics serialise across the chip's XCDs): every split
+//    writes its (m, l, o) record with device-scope stores and then a ready flag
+//    for each merger.  The mergers are the last (up to four) splits of the
+//    (sequence, kv head) - the highest workgroup indices of the group, so they
+//    only wait on workgroups dispatched before them or on each other, and
+//    there are never more of them than the chip holds at once.  Each polls its
+//    flags with a bounded spin, combines its share of the output columns and
+//    clears its own flag row for the next call.
 #include "common.hpp"
 #include "device.hpp"
 
@@ -36,14 +38,15 @@ namespace gqa {
 
 namespace {
 
+#ifndef GQA_DECODE_BATCH
+#define GQA_DECODE_BATCH 2                 // pages a wave keeps in flight
+#endif
 constexpr int kSpinLimit = 1 << 18;        // bounded wait for a split's flag
+constexpr int kMergeBatch = 8;             // split records a merging thread loads at once
+constexpr int kSc1 = 16;                   // buffer cache policy: sc1 (device-scope coherent)
+constexpr int kBufferWord3 = 0x00020000;   // buffer resource word 3: raw 32-bit dword access
 
-__device__ __forceinline__ void store_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_dev(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 }  // namespace
 
@@ -51,12 +54,9 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NQ = D / 32;      // k-steps of the score product
   constexpr int NDB = D / 16;     // 16-row blocks of the output
-  constexpr int kRec = D + 4;     // partial record: o[D], m, l, pad
   __shared__ float red_m[4][16];
   __shared__ float red_l[4][16];
   __shared__ float red_o[4][16][D + 4];
-  __shared__ float s_w[16][kMaxSplitDecode];
-  __shared__ float s_M[16];
   __shared__ int s_ok;
 
   const int G = a.Hq / a.Hkv;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   // the block-table entries of this wave's pages, the query, its rotation row
   // and the new token.  Loads are unconditional (indices clamped to valid
   // rows) so the compiler issues them back to back.
-  constexpr int kBatch = 4;
+  constexpr int kBatch = GQA_DECODE_BATCH;
   const int p_first = p_begin + wave;
   int64_t phys[kBatch];
 #pragma unroll
@@ -289,7 +289,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) red_o[wave][c16][db * 16 + grp * 4 + i] = o[db][i];
   __syncthreads();
 
-  // 256 threads: head column hh = tid / 16, 16 threads per head over d
+  // 256 threads: head column hh = tid / 16; thread dl holds d = E*dl .. E*dl + E-1
+  constexpr int E = D / 16;
   const int hh = threadIdx.x >> 4;
   const int dl = threadIdx.x & 15;
   const bool hv2 = hh < Gc;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
   for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
   float L = 0.f;
-  float acc[D / 16];
+  float acc[E];
   {
     float sc[4];
 #pragma unroll
@@ -307,101 +308,133 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
       L += red_l[w][hh] * sc[w];
     }
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) {
+    for (int e = 0; e < E; ++e) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v += red_o[w][hh][dl + 16 * k] * sc[w];
-      acc[k] = v;
+      for (int w = 0; w < 4; ++w) v += red_o[w][hh][E * dl + e] * sc[w];
+      acc[e] = v;
     }
   }
-  uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(h2) * a.o_s1;
   if (nsplit == 1) {
     if (!hv2) return;
     const float inv = 1.f / L;
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(h2) * a.o_s1;
+    uint32_t w[E / 2];
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) orow[dl + 16 * k] = f32_to_bf16(acc[k] * inv);
+    for (int e = 0; e < E / 2; ++e) w[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    if constexpr (E == 8)
+      *reinterpret_cast<u32x4*>(orow + E * dl) = u32x4{w[0], w[1], w[2], w[3]};
+    else
+      *reinterpret_cast<u32x2*>(orow + E * dl) = u32x2{w[0], w[1]};
     return;
   }
 
-  // partial records of this (sequence, blockIdx.y): [split][head in chunk][kRec]
+  // Split records of this (sequence, blockIdx.y): o rows [split][head in chunk][D]
+  // and (m, l) headers [split][head in chunk], written and read with
+  // device-scope (sc1) buffer accesses, which stay coherent across the XCDs'
+  // L2 caches.  The last K splits are also mergers: merger j combines output
+  // columns [j*D/K, (j+1)*D/K) of every head.  Flags: one row of nsplit per
+  // merger, so a merger clears its own row without racing another's wait.
+  const int K = nsplit >= kDecodeMergers ? kDecodeMergers : 2;   // divides D/4
+  const int mj = split - (nsplit - K);          // merger index, negative for the others
   const int64_t group = static_cast<int64_t>(a.split_off[b]) * gy + static_cast<int64_t>(blockIdx.y) * nsplit;
-  float* region = a.part_o + group * (16 * kRec);
-  int32_t* flags = a.flags + group;
-  if (split != nsplit - 1) {
-    if (hv2) {
-      float* rec = region + (static_cast<int64_t>(split) * Gc + hh) * kRec;
+  int32_t* flags = a.flags + group * kDecodeMergers;
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o + group * (16 * D), 0, nsplit * Gc * D * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rh =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_h + group * (16 * 2), 0, nsplit * Gc * 2 * 4, kBufferWord3);
+  if (hv2) {
+    const int rec = split * Gc + hh;
 #pragma unroll
-      for (int k = 0; k < D / 16; ++k) store_dev(rec + dl + 16 * k, acc[k]);
-      if (dl == 0) {
-        store_dev(rec + D, M);
-        store_dev(rec + D + 1, L);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);      // this thread's record has reached the device
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flags + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
+    for (int e = 0; e < E; e += 4)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]}), ro,
+          (rec * D + E * dl + e) * 4, 0, kSc1);
+    if (dl == 0) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, float2_t{M, L}), rh, rec * 8, 0, kSc1);
   }
-
-  // the last split: wait for the others (bounded), then combine
-  const int others = nsplit - 1;
-  if (threadIdx.x == 0) s_ok = 1;
+  __builtin_amdgcn_s_waitcnt(0);        // this thread's record has reached the device
   __syncthreads();
-  for (int t = threadIdx.x; t < others; t += 256) {
+  if (static_cast<int>(threadIdx.x) < K && static_cast<int>(threadIdx.x) != mj)
+    __hip_atomic_store(flags + threadIdx.x * nsplit + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (mj < 0) return;
+
+  // Merger: wait (bounded) for every other split's record.  Then each of this
+  // merger's (head, column) pairs is spread over F adjacent lanes (F a power
+  // of two), lane f taking splits f, f + F, ...: a few loads per thread, all in
+  // flight together, a register-only combine with a running maximum, and the F
+  // partials combined across lanes.
+  int32_t* myflags = flags + mj * nsplit;
+  if (threadIdx.x == 0) s_ok = 1;
+  for (int t = threadIdx.x; t < nsplit; t += 256) {
+    if (t == split) continue;
     int spins = 0;
-    while (__hip_atomic_load(flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && spins < kSpinLimit) {
+    while (__hip_atomic_load(myflags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && spins < kSpinLimit) {
       __builtin_amdgcn_s_sleep(2);
       ++spins;
     }
     if (spins >= kSpinLimit) s_ok = 0;
   }
   __syncthreads();
-  // maxima of every split (its own included) and their weights
-  for (int r = threadIdx.x; r < others * Gc; r += 256) {
-    const int sp = r / Gc;
-    const int hl3 = r - sp * Gc;
-    s_w[hl3][sp] = load_dev(region + static_cast<int64_t>(r) * kRec + D);
-  }
-  if (dl == 0 && hv2) s_w[hh][others] = M;
-  __syncthreads();
-  if (threadIdx.x < Gc) {
-    float mm = -INFINITY;
-    for (int sp = 0; sp <= others; ++sp) mm = fmaxf(mm, s_w[threadIdx.x][sp]);
-    s_M[threadIdx.x] = mm;
-  }
-  __syncthreads();
-  if (hv2) {
-    const float Mg = s_M[hh];
-    const float wown = __builtin_amdgcn_exp2f(M - Mg);
-    float Lg = L * wown;
+  const int CK = (D / 4) / K;              // float4 columns of a head owned by this merger
+  const int P = Gc * CK;                   // (head, column) pairs, at most 256
+  int F = 1;                               // lanes per pair: largest power of two with P*F <= 256, at most 16
+  while (F < 16 && P * F * 2 <= 256) F *= 2;
+  const int t = threadIdx.x;
+  const int pr = t / F;
+  const int f = t & (F - 1);
+  const bool pv = pr < P;
+  const int ph = pv ? pr / CK : 0;
+  const int pc = mj * CK + pr % CK;
+  float Mr = -INFINITY;
+  float Lr = 0.f;
+  f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+  if (pv) {
+    for (int s0 = f; s0 < nsplit; s0 += F * kMergeBatch) {
+      float2_t hm[kMergeBatch];
+      f32x4 v[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) acc[k] *= wown;
-    for (int s0 = 0; s0 < others; s0 += 8) {
-      float v[8][D / 16 + 1];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float* rec = region + (static_cast<int64_t>(min(s0 + u, others - 1)) * Gc + hh) * kRec;
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k) v[u][k] = load_dev(rec + dl + 16 * k);
-        v[u][D / 16] = load_dev(rec + D + 1);
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int rec = min(s0 + u * F, nsplit - 1) * Gc + ph;
+        hm[u] = __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(rh, rec * 8, 0, kSc1));
+        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (rec * D + 4 * pc) * 4, 0, kSc1));
       }
+      // s0 < nsplit, so hm[0] is valid and mx is finite
+      float mx = Mr;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (s0 + u < others) {
-          const float w = __builtin_amdgcn_exp2f(s_w[hh][s0 + u] - Mg);
+      for (int u = 0; u < kMergeBatch; ++u) mx = fmaxf(mx, s0 + u * F < nsplit ? hm[u].x : -INFINITY);
+      const float sc = __builtin_amdgcn_exp2f(Mr - mx);
+      acc4 *= sc;
+      Lr *= sc;
+      Mr = mx;
 #pragma unroll
-          for (int k = 0; k < D / 16; ++k) acc[k] += v[u][k] * w;
-          Lg += v[u][D / 16] * w;
-        }
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float e = __builtin_amdgcn_exp2f(hm[u].x - mx);
+        const float w = s0 + u * F < nsplit ? e : 0.f;
+        acc4 += v[u] * w;
+        Lr += hm[u].y * w;
       }
     }
-    const float inv = s_ok ? 1.f / Lg : __builtin_nanf("");
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) orow[dl + 16 * k] = f32_to_bf16(acc[k] * inv);
   }
-  // leave every flag of the group at zero for the next call
-  for (int t = threadIdx.x; t < others; t += 256)
-    __hip_atomic_store(flags + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // combine the F lanes of each pair (a lane that took no split holds m = -inf, l = 0)
+  float Mg = Mr;
+  for (int x = 1; x < F; x <<= 1) Mg = fmaxf(Mg, __shfl_xor(Mg, x));
+  const float w = Mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mr - Mg);
+  float Lg = Lr * w;
+  f32x4 o4 = acc4 * w;
+  for (int x = 1; x < F; x <<= 1) {
+    Lg += __shfl_xor(Lg, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] += __shfl_xor(o4[e], x);
+  }
+  if (pv && f == 0) {
+    const float inv = s_ok ? 1.f / Lg : __builtin_nanf("");
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(g * G + hcb * 16 + ph) * a.o_s1;
+    *reinterpret_cast<u32x2*>(orow + 4 * pc) =
+        u32x2{pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv)};
+  }
+  // leave this merger's flag row at zero for the next call
+  for (int t = threadIdx.x; t < nsplit; t += 256)
+    if (t != split) __hip_atomic_store(myflags + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s) {

@@ -476,3 +476,35 @@ def test_decode_step_fused(Hq, Hkv, lengths):
         kb, vb = b.gpu.gather(s, 0)
         assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
         assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [40000, 16 * 16 * 4 + 1, 16 * 16 * 4])
+def test_decode_many_splits(T):
+    """One long sequence on one kv head: up to 125 splits, several merge rounds
+    per lane (running maximum across rounds), and 4- and 5-split merges."""
+    say(f"case: decode_step with many splits, T={T}, Hq=8 Hkv=1 d=128")
+    import causal_gqa_attention_attn_amd as lib
+    from oracle.cache_model import CacheModel
+    pages = -(-T // 16) + 2
+    cache = lib.PagedCache(1, 1, 128, pages, 1, pages, dtype=torch.bfloat16, rope_theta=1e4,
+                           max_position=pages * 16, free_list_order=W.page_order(pages, 77))
+    kf = W.normal_device((1, 1, T - 1, 128), 93000 + T)
+    vf = W.normal_device((1, 1, T - 1, 128), 94000 + T)
+    lib.kv_cache_append(cache.handle, 0, [0], kf, vf, torch.ones((1, T - 1), dtype=torch.uint8),
+                        torch.arange(T - 1, dtype=torch.int32)[None])
+    shape = W.AttnShape(B=1, n=1, Hq=8, Hkv=1, d=128, dtype=torch.bfloat16, theta=1e4)
+    st = W.decode_step_inputs(shape, 95, T)
+    o = torch.full((1, 8, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(lib.gqa_workspace_size(cache.handle, 1, 8), dtype=torch.uint8, device="cuda")
+    for rep in range(2):                      # second call: flags were left at zero
+        if rep:
+            lib.kv_cache_truncate(cache.handle, 0, T - 1)
+        lib.gqa_decode_step(cache.handle, 0, [0], st.q.cuda(), st.k.cuda(), st.v.cuda(), o, ws)
+        torch.cuda.synchronize()
+        ref = CacheModel(1, 1, 128, 16, pages, 1, pages, dtype="bf16", rope_theta=1e4, max_position=pages * 16)
+        k = torch.cat([kf.cpu(), st.k], dim=2)
+        v = torch.cat([vf.cpu(), st.v], dim=2)
+        ref.append(0, [0], as_f32(k), as_f32(v), np.ones((1, T), np.uint8), np.arange(T)[None])
+        r = ref.decode(0, [0], as_f32(st.q), [T])
+        compare_rows(o, r, torch.bfloat16)
+    cache.close()
