@@ -79,10 +79,11 @@ __global__ __launch_bounds__(256, R == 1 ? 2 : 1) void prefill_bf16_kernel(AttnA
   constexpr int PER_T = KCH / 256;     // chunks per thread
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * S::BUF];
 
+  // kv head fastest: with 8 kv heads, block i lands on XCD i % 8 = its kv head,
+  // so each XCD's L2 holds the keys and values of one head
   const int G = a.Hq / a.Hkv;
-  const int nchunk = G / Gc;
-  const int g = blockIdx.x / nchunk;
-  const int hc = blockIdx.x - g * nchunk;
+  const int hc = blockIdx.x / a.Hkv;
+  const int g = blockIdx.x - hc * a.Hkv;
   const int b = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
   const int Tq = 32 * TB;
