@@ -17,11 +17,19 @@ prefill throughput 2*B*Hq*n^2*d / (append + attention time, HIP events);
 ``decode`` reports the decode KV-read rate over the 64 layers.  ``roofline``
 is the prefill attention kernel: algorithmic flops of one launch over its
 event-timed duration, against the bf16 dense MFMA peak; ``roofline_decode``
-is one layer of the decode graph (append, split and merge kernels) against
-HBM.  ``cpu_baseline`` times the float64 oracle on a bounded sample of the
+is one layer of the decode graph (one decode_bf16_kernel launch: append,
+split-T attention and split combine) against HBM.  ``cpu_baseline`` times the float64 oracle on a bounded sample of the
 same prefill (query rows spread over the sequence) on this host's cores.
+``other_configs`` reports the other measured configurations on the same
+GPU, each timed with HIP events (median of 20 after 3 warm-ups):
+  * Llama-shaped prefill: B=8, n=2048, Hq=32, Hkv=8, d=128 (gqa_prefill);
+  * serving decode: one gqa_decode_step of 64 sequences with lengths
+    log-uniform in [512, 32768] on one layer (about 2.2 GB of K/V);
+  * edit re-prefill: 16 sequences of 4096 tokens, each truncated at a seeded
+    m_b and its suffix re-prefilled (gqa_prefill on a non-empty cache);
+    flops 2*Hq*d*(n^2 - m_b^2).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-other-configs]
 """
 import argparse
 import hashlib
@@ -94,6 +102,100 @@ def cpu_baseline(inp, budget_s):
                       f"spread over the sequence, heaviest first), float64 numpy, {t_used:.1f} s"}
 
 
+def _median_ms(fn, before=None, iters=20, warm=3):
+    """Median and minimum event time of fn(); before() runs untimed each time."""
+    import torch
+    for _ in range(warm):
+        if before:
+            before()
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(iters):
+        if before:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def other_configs(lib, W):
+    import torch
+    res = {}
+    # Llama-shaped prefill
+    inp = W.llama()
+    Q, K, V = inp.Q.cuda(), inp.K.cuda(), inp.V.cuda()
+    O = torch.empty_like(Q)
+    sh = W.LLAMA
+    pre = lib.PagedCache(1, sh.Hkv, sh.d, sh.B * (sh.n // 16) + 16, sh.B, sh.n // 16 + 2, dtype=torch.bfloat16,
+                         rope_theta=sh.theta, max_position=sh.n + 32)
+    ids = list(range(sh.B))
+    med, mn = _median_ms(lambda: lib.gqa_prefill(pre.handle, 0, ids, Q, K, V, inp.mask, inp.positions, O),
+                         before=lambda: [lib.kv_cache_truncate(pre.handle, b, 0) for b in ids])
+    flops = sum(2.0 * sh.Hq * sh.d * n * n for n in inp.lengths)
+    res["llama_prefill"] = {"workload": "causal prefill B=8 n=2048 Hq=32 Hkv=8 d=128 (gqa_prefill)",
+                            "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+                            "frac": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                            "ms_median": round(med, 4), "ms_min": round(mn, 4)}
+    pre.close()
+    del Q, K, V, O
+    # serving decode
+    lens = W.serving_lengths()
+    Bs = len(lens)
+    sh = W.SERVING
+    pages = sum(-(-(x + 1) // 16) for x in lens) + 8
+    cache = lib.PagedCache(1, sh.Hkv, sh.d, pages, Bs, 32768 // 16 + 2, dtype=torch.bfloat16, rope_theta=sh.theta,
+                           max_position=32770, free_list_order=W.page_order(pages, 1005))
+    for b, L in enumerate(lens):
+        kf = W.normal_device((1, sh.Hkv, L, sh.d), 91000 + b)
+        vf = W.normal_device((1, sh.Hkv, L, sh.d), 92000 + b)
+        lib.kv_cache_append(cache.handle, 0, [b], kf, vf, torch.ones((1, L), dtype=torch.uint8),
+                            torch.arange(L, dtype=torch.int32)[None])
+    st = W.decode_step_inputs(sh, 1005, 0)
+    q, k, v = st.q.cuda(), st.k.cuda(), st.v.cuda()
+    o = torch.empty_like(q)
+    ws = torch.zeros(lib.gqa_workspace_size(cache.handle, Bs, sh.Hq), dtype=torch.uint8, device="cuda")
+    ids = list(range(Bs))
+    med, mn = _median_ms(lambda: lib.gqa_decode_step(cache.handle, 0, ids, q, k, v, o, ws),
+                         before=lambda: [lib.kv_cache_truncate(cache.handle, b, lens[b]) for b in ids])
+    nbytes = sum((L + 1) * 2 * sh.Hkv * sh.d * 2 for L in lens)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    res["serving_decode"] = {"workload": "gqa_decode_step of 64 sequences, lengths log-uniform [512, 32768], "
+                                         "Hq=32 Hkv=8 d=128, one layer",
+                             "kv_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1)}
+    cache.close()
+    # edit re-prefill
+    sh = W.EDIT
+    full = W.prefill_inputs(sh, 1006)
+    ms = W.edit_points(sh.B, sh.n)
+    lens = [sh.n - m for m in ms]
+    suffix = W.prefill_inputs(W.AttnShape(B=sh.B, n=max(lens), Hq=sh.Hq, Hkv=sh.Hkv, d=sh.d, dtype=sh.dtype,
+                                          theta=sh.theta), 2006, lengths=lens, start=ms)
+    cache = lib.PagedCache(1, sh.Hkv, sh.d, sh.B * (sh.n // 16) + 16, sh.B, sh.n // 16 + 2, dtype=torch.bfloat16,
+                           rope_theta=sh.theta, max_position=sh.n + 32)
+    ids = list(range(sh.B))
+    Of = torch.empty((sh.B, sh.Hq, sh.n, sh.d), dtype=torch.bfloat16, device="cuda")
+    lib.gqa_prefill(cache.handle, 0, ids, full.Q.cuda(), full.K.cuda(), full.V.cuda(), full.mask, full.positions, Of)
+    Qs, Ks, Vs = suffix.Q.cuda(), suffix.K.cuda(), suffix.V.cuda()
+    Os = torch.empty_like(Qs)
+    med, mn = _median_ms(lambda: lib.gqa_prefill(cache.handle, 0, ids, Qs, Ks, Vs, suffix.mask, suffix.positions, Os),
+                         before=lambda: [lib.kv_cache_truncate(cache.handle, b, m) for b, m in zip(ids, ms)])
+    flops = sum(2.0 * sh.Hq * sh.d * (sh.n * sh.n - m * m) for m in ms)
+    res["edit_reprefill"] = {"workload": "16 x 4096 cached, truncate at seeded m_b, re-prefill the suffix "
+                                         "(gqa_prefill), Hq=32 Hkv=8 d=128",
+                             "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+                             "frac": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                             "ms_median": round(med, 4), "ms_min": round(mn, 4)}
+    cache.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +204,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (profiling aid)")
+    ap.add_argument("--no-other-configs", action="store_true", help="skip the Llama, serving and edit measurements")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device 5 times (calibrates rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -245,6 +348,9 @@ def main():
                                   "kernel": "one layer of the replayed decode graph: decode_bf16_kernel<128> "
                                             "(append, split-T attention and split combine), 32 MiB of K/V",
                                   "layer_us": round(per_layer_ms * 1e3, 2)}
+    if not args.no_other_configs and not args.prefill_only:
+        print("bench: other configurations", file=sys.stderr, flush=True)
+        out["other_configs"] = other_configs(lib, W)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

@@ -63,7 +63,7 @@ gqa_status fail(gqa_status s, const std::string& msg) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 #ifndef GQA_DECODE_TARGET_BLOCKS
-#define GQA_DECODE_TARGET_BLOCKS 1024
+#define GQA_DECODE_TARGET_BLOCKS 4096
 #endif
 #ifndef GQA_DECODE_MIN_PAGES
 #define GQA_DECODE_MIN_PAGES 16
