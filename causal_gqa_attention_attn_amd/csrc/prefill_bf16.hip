@@ -449,7 +449,9 @@ __global__ __launch_bounds__(256, R == 1 ? 2 : 1) void prefill_bf16_kernel(AttnA
 }
 
 // Heads per workgroup (Gc, dividing G) and 32-token blocks per workgroup (TB)
-// with Gc * TB = 4 * R: three row-blocks per wave when the group size allows,
+// with Gc * TB = 4 * R and TB >= GQA_PREFILL_MIN_TB (two 32-token blocks:
+// 64-token query tiles match the 64-key tiles, which keeps the diagonal's
+// masked work small): three row-blocks per wave when the group size allows,
 // else two, else one.
 struct PrefillShape {
   int Gc, TB, R;
@@ -459,10 +461,14 @@ struct PrefillShape {
 #define GQA_PREFILL_MAX_R 1
 #endif
 
+#ifndef GQA_PREFILL_MIN_TB
+#define GQA_PREFILL_MIN_TB 2
+#endif
+
 static PrefillShape prefill_shape(int G) {
   for (int R = GQA_PREFILL_MAX_R; R >= 1; --R)
     for (int Gc = G; Gc >= 1; --Gc)
-      if (G % Gc == 0 && (4 * R) % Gc == 0) return {Gc, 4 * R / Gc, R};
+      if (G % Gc == 0 && (4 * R) % Gc == 0 && 4 * R / Gc >= GQA_PREFILL_MIN_TB) return {Gc, 4 * R / Gc, R};
   return {1, 4, 1};
 }
 
