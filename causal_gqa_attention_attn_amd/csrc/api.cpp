@@ -81,6 +81,10 @@ gqa_status check_config(const gqa_cache_config* c) {
   if (c->head_dim < 1 || c->head_dim > 128) return fail(GQA_ERR_UNSUPPORTED, "head_dim must be 1..128");
   if (c->dtype == GQA_BF16 && c->head_dim != 64 && c->head_dim != 128)
     return fail(GQA_ERR_UNSUPPORTED, "bf16 caches need head_dim 64 or 128");
+  // the bf16 kernels address one layer of a pool with 32-bit byte offsets
+  if (c->dtype == GQA_BF16 &&
+      static_cast<int64_t>(c->num_pages) * c->num_kv_heads * kPage * c->head_dim * 2 > 0xffffffffLL)
+    return fail(GQA_ERR_UNSUPPORTED, "one layer of a bf16 pool must stay below 4 GiB");
   if (c->rope_style != 0 && c->rope_style != 1) return fail(GQA_ERR_UNSUPPORTED, "rope_style must be 0 or 1");
   if (c->rope_style == 1) {
     if (c->head_dim % 2) return fail(GQA_ERR_ARG, "rotation needs an even head_dim");
@@ -314,6 +318,7 @@ gqa_status launch_attention(gqa_cache* c, int32_t layer, int32_t B, const int32_
     a.nseq = nb;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
+    a.pool_bytes = static_cast<uint32_t>(c->layer_elems * c->elt);
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
     for (int j = 0; j < nb; ++j) {
       const int b = b0 + j;

@@ -61,6 +61,7 @@ struct AttnArgs {
   int32_t Hq, Hkv, d, n_rect, nseq;
   float scale;                // 1/sqrt(d)
   float scale_log2;           // log2(e)/sqrt(d)
+  uint32_t pool_bytes;        // bytes of this layer's K (= V) pool; offsets into it fit 32 bits
   const float* rope;
   SeqMeta meta;
 };

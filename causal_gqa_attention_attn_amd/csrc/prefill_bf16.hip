@@ -10,38 +10,42 @@
 //
 // How (a gfx950 design, not a translation of any page's kernel):
 //  * one workgroup = 4 waves, one per SIMD, for (kv head g, a chunk of Gc of
-//    its query heads, sequence, Tq query tokens).  Its Gc*Tq query rows form
-//    row-blocks of 32 (one head, 32 tokens); each wave owns R of them, so every
-//    K/V fragment it reads from LDS feeds R matrix-core products, and every K/V
-//    tile staged in LDS serves all Gc query heads of the group (the head map is
-//    an index; the cache is never replicated);
-//  * S^T = K q^T on v_mfma_f32_32x32x16_bf16 with keys as rows: each lane owns
-//    one query column, so row maxima and sums stay in a lane plus one exchange
-//    with the lane 32 away;
-//  * K rows are fed to the matrix core in a fixed permutation so the score
-//    accumulator already has the register layout of the B operand of
-//    O^T += V^T P^T (no shuffle of P); V pages are stored d-major, so V^T tiles
-//    are staged with plain 16-byte copies;
-//  * 64-key K/V tiles are double-buffered in LDS: the next tile's global loads
-//    are in flight while the current one is used, one barrier per tile;
-//  * softmax in base 2 with the 1/sqrt(d)*log2(e) scale folded into one
-//    multiply-add, against a fixed reference per query row: the maximum of the
-//    row's first 32-key sub-tile (which always holds key 0, visible to every
-//    query, so the reference is finite and a fully masked later tile never
-//    meets (-inf) - (-inf)).  Unnormalised probabilities 2^(s - ref) and their
-//    sums stay exact in float32/bf16 range while no score exceeds the
-//    reference by more than 2^64, so the output accumulators are never
-//    rescaled in the loop.  Each lane records its largest score; if any lane
-//    of the workgroup passes that bound, the workgroup runs the tile loop once
-//    more with the recorded maxima as references, which cannot overflow;
-//  * key tiles wholly in the future of a workgroup are never loaded; 32-key
-//    sub-tiles wholly in the future of a row-block are skipped; masking by
-//    select happens only on tiles that cross the diagonal;
-//  * slots at or beyond the written length are zero-filled in LDS, so stale or
-//    poisoned cache memory never meets a zero weight (0 * NaN);
-//  * workgroups are dispatched heaviest (last) query tile first.
-#include <type_traits>
-
+//    its query heads, sequence, 32*TB query tokens) with Gc*TB = 4: each wave
+//    owns one row-block of 32 queries of one head, and every K/V tile staged
+//    in LDS serves all Gc query heads of the group (the head map is an index;
+//    the cache is never replicated).  Two workgroups share a CU, so each SIMD
+//    runs two waves whose matrix-core and vector work interleave;
+//  * 64-key K/V tiles (four pages) go from HBM straight into LDS with 16-byte
+//    buffer loads (no staging registers, no per-tile address arithmetic: wave
+//    w loads page w of the tile, the page offset is a scalar and every lane's
+//    offset inside the page is fixed).  The LDS layouts are page-major and put
+//    the 16 lanes of one read on 16 consecutive 16-byte chunks, so matrix-core
+//    operand reads are free of bank conflicts;
+//  * S^T = K q^T on v_mfma_f32_32x32x16_bf16 with keys as rows, so each lane
+//    owns one query column; K rows are fed in a fixed permutation that makes
+//    the score accumulator the B operand of O^T += V^T P^T as it stands, and
+//    V pages are stored d-major so V^T operands are plain 16-byte reads;
+//  * software pipeline: K runs one tile ahead of V, so while the softmax of
+//    tile j runs on the vector unit the scores of tile j+1 run on the matrix
+//    core; loads of K(j+2) and V(j+1) are in flight during tile j, and one
+//    barrier per tile retires them;
+//  * softmax in base 2 against a fixed reference per query row: the maximum
+//    of the row's first 32 keys (key 0 is visible to every query, so the
+//    reference is finite and a masked key never meets (-inf) - (-inf)).  The
+//    loop keeps no running maximum and never rescales; the probabilities are
+//    rounded to bf16 once, and their row sums are taken from those bf16 values
+//    with dot2 instructions.  A row whose sum passes 2^64 (some score beyond
+//    the reference by more than 2^64 in probability) makes the workgroup find
+//    the exact row maxima in a score-only pass and run again against them,
+//    which cannot overflow;
+//  * key tiles wholly in the future of the workgroup are never loaded;
+//    masking by select happens only on tiles that cross the diagonal;
+//  * value slots at or beyond the written length are zeroed in LDS by the
+//    wave that loaded them, so stale or poisoned cache memory never meets a
+//    zero weight (0 * NaN); stale keys only reach masked scores;
+//  * workgroups are dispatched heaviest (last) query tile first, kv head
+//    fastest, so with 8 kv heads workgroup i lands on XCD i % 8 = its kv head
+//    and each XCD's L2 serves one head's keys and values.
 #include "common.hpp"
 #include "device.hpp"
 
@@ -49,45 +53,57 @@ namespace gqa {
 
 namespace {
 
-// Key (or head-dim) row fed to MFMA row r: keeps the accumulator of rows
-// 8*(i/4) + 4*half + i%4 equal to keys 16*(i/8) + 8*half + i%8.
-__device__ __forceinline__ int perm32(int r) {
-  return ((r >> 4) << 4) + (((r >> 2) & 1) << 3) + (((r >> 3) & 1) << 2) + (r & 3);
+constexpr int KT = 64;                 // keys per tile (four 16-slot pages)
+
+// Swaps bits 2 and 3 (an involution).  MFMA row r is fed key (or d-row)
+// perm32(r), which keeps the accumulator of rows 8*(i/4) + 4*half + i%4 equal
+// to keys 16*(i/8) + 8*half + i%8.
+__device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer descriptor of a byte range (reads past num_records return zero).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int>(p), static_cast<int>((p >> 32) & 0xffff), static_cast<int>(bytes), 0x00020000};
 }
 
-constexpr int KT = 64;                 // keys per staged tile
-
-template <int D>
-struct Smem {
-  static constexpr int KPAD = D + 8;   // LDS row stride of K (elements)
-  static constexpr int VPAD = KT + 8;  // LDS row stride of V^T
-  static constexpr int K_ELEMS = KT * KPAD;
-  static constexpr int V_ELEMS = D * VPAD;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
-};
+// 16 bytes per lane from buffer r at byte (voff + soff) into LDS byte
+// lds_addr + 16*lane.  Written as one instruction so that the compiler does
+// not order LDS reads of other buffers behind these loads; the caller waits
+// (s_waitcnt vmcnt) and synchronises before the data is read.
+__device__ __forceinline__ void dma16(i32x4 r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff));
+}
 
 }  // namespace
 
-// Template R: row-blocks per wave.  Runtime Gc (heads per workgroup) and TB
-// (32-token blocks per workgroup) satisfy Gc * TB == 4 * R.
-template <int D, int R>
-__global__ __launch_bounds__(256, R == 1 ? 2 : 1) void prefill_bf16_kernel(AttnArgs a, int Gc, int TB) {
-  using S = Smem<D>;
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc, int TB) {
   constexpr int NC = D / 16;           // k-steps of the score product
   constexpr int NDB = D / 32;          // 32-row blocks of the output
-  constexpr int KCH = KT * D / 8;      // 16-byte chunks of a K (or V) tile
-  constexpr int PER_T = KCH / 256;     // chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * S::BUF];
+  constexpr int PCH = 2 * D;           // 16-byte chunks of one (page, kv head) of K or of V
+  constexpr int NI = PCH / 64;         // buffer-to-LDS loads per wave per tile, for K and for V
+  constexpr int TEL = KT * D;          // elements of a K or V tile
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TEL];   // K tiles 0, 1; V tiles 0, 1
 
-  // kv head fastest: with 8 kv heads, block i lands on XCD i % 8 = its kv head,
-  // so each XCD's L2 holds the keys and values of one head
   const int G = a.Hq / a.Hkv;
   const int hc = blockIdx.x / a.Hkv;
   const int g = blockIdx.x - hc * a.Hkv;
   const int b = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
   const int Tq = 32 * TB;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
@@ -99,8 +115,9 @@ __global__ __launch_bounds__(256, R == 1 ? 2 : 1) void prefill_bf16_kernel(AttnA
   const int total = a.meta.total[b];
   const int h0 = g * G + hc * Gc;      // first query head of this workgroup
 
-  // padding rows of this workgroup's rectangular range -> 0
-  {
+  // padding rows of this workgroup's rectangular range -> 0 (after every
+  // page-table read, so those reads may use the scalar cache)
+  auto zero_padding = [&]() {
     const int rlo = tile * Tq;
     const int rhi = min(a.n_rect, rlo + Tq);
     const int per_row = D / 8;
@@ -116,44 +133,39 @@ __global__ __launch_bounds__(256, R == 1 ? 2 : 1) void prefill_bf16_kernel(AttnA
         *reinterpret_cast<u32x4*>(op) = z;
       }
     }
-  }
+  };
 
   const int t0 = tile * Tq;
-  if (t0 >= nb) return;
+  if (t0 >= nb) {
+    zero_padding();
+    return;
+  }
   const int qn = min(Tq, nb - t0);
 
-  // this wave's row-blocks: head, first token, validity
-  int rb_h[R], rb_t[R];
-  bool rb_ok[R];
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int rb = wave * R + j;
-    rb_h[j] = h0 + rb / TB;
-    rb_t[j] = (rb % TB) * 32;          // token offset inside the tile
-    rb_ok[j] = rb_t[j] < qn;
-  }
+  // this wave's row-block: head, first token, validity; the lane's query
+  const int rb_h = h0 + wave / TB;
+  const int rb_t = (wave % TB) * 32;
+  const bool q_ok = rb_t + col < qn;
+  const int qpos = c0 + t0 + rb_t + col;
 
   // rotated queries as B operands: lane holds dims 16c + 8*half + 0..7 of its query
-  bf16x8 qf[R][NC];
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int t = t0 + rb_t[j] + col;
-    const bool qv = rb_ok[j] && (rb_t[j] + col < qn);
+  bf16x8 qf[NC];
+  {
     float x[NC][8];
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.q_s0 + static_cast<int64_t>(rb_h[j]) * a.q_s1 +
-                           static_cast<int64_t>(r0 + t) * a.q_s2;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.q_s0 + static_cast<int64_t>(rb_h) * a.q_s1 +
+                           static_cast<int64_t>(r0 + t0 + rb_t + col) * a.q_s2;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qv) w = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
+      if (q_ok) w = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[c][2 * e] = __uint_as_float(w[e] << 16);
         x[c][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
       }
     }
-    if (a.rope && qv) {
-      const float* rrow = a.rope + static_cast<int64_t>(c0 + t) * D;    // (D/2) (cos, sin) pairs
+    if (a.rope && q_ok) {
+      const float* rrow = a.rope + static_cast<int64_t>(qpos) * D;    // (D/2) (cos, sin) pairs
 #pragma unroll
       for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
@@ -166,310 +178,321 @@ __global__ __launch_bounds__(256, R == 1 ? 2 : 1) void prefill_bf16_kernel(AttnA
         }
     }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x4 w;
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[c][2 * e], x[c][2 * e + 1]);
-      qf[j][c] = __builtin_bit_cast(bf16x8, w);
-    }
+      for (int e = 0; e < 8; ++e) qf[c][e] = static_cast<__bf16>(x[c][e]);
   }
 
   const int kv_end = c0 + t0 + qn;            // keys [0, kv_end) can be visible
   const int ntk = (kv_end + KT - 1) / KT;
-  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+  const int last_page = (total - 1) >> 4;
   const int32_t* trow = a.table + static_cast<int64_t>(seq) * a.table_w;
   const int Hkv = a.Hkv;
   const float sl2 = a.scale_log2;
+  const i32x4 krs = make_rsrc(a.k_pool, a.pool_bytes);
+  const i32x4 vrs = make_rsrc(a.v_pool, a.pool_bytes);
 
-  // ---- global -> registers -> LDS staging of one K/V tile.  The tile's
-  // four pages are looked up once; a thread's 16-byte chunks fall in known
-  // pages, so all its loads issue back to back.  Slots at or past the written
-  // length read a valid page and are zeroed afterwards (no branches).
-  const int last_page = (total - 1) >> 4;
-  u32x4 stg[2 * PER_T];
-  auto load_tile = [&](int kt) {
-    const int kbase = kt * KT;
-    int64_t phys[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) phys[p] = trow[min(kt * 4 + p, last_page)];
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ci = threadIdx.x + 256 * i;
-      const int kl = ci / (D / 8);
-      const int ch = ci - kl * (D / 8);
-      const int pl = kl >> 4;
-      const int64_t ph = pl == 0 ? phys[0] : pl == 1 ? phys[1] : pl == 2 ? phys[2] : phys[3];
-      stg[i] = *reinterpret_cast<const u32x4*>(kpool + ((ph * Hkv + g) * kPage + (kl & 15)) * D + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ci = threadIdx.x + 256 * i;
-      const int pl = ci / (D * 2);
-      const int rem = ci - pl * (D * 2);
-      const int dd = rem >> 1;
-      const int h8 = rem & 1;
-      const int64_t ph = pl == 0 ? phys[0] : pl == 1 ? phys[1] : pl == 2 ? phys[2] : phys[3];
-      stg[PER_T + i] = *reinterpret_cast<const u32x4*>(vpool + ((ph * Hkv + g) * D + dd) * kPage + h8 * 8);
-    }
-    if (kbase + KT > total) {            // the tile holds the end of the sequence
-#pragma unroll
-      for (int i = 0; i < PER_T; ++i) {
-        const int ci = threadIdx.x + 256 * i;
-        const int key = kbase + ci / (D / 8);
-        if (key >= total) stg[i] = u32x4{0u, 0u, 0u, 0u};
-        const int pl = ci / (D * 2);
-        const int h8 = (ci - pl * (D * 2)) & 1;
-        const int key0 = kbase + pl * 16 + h8 * 8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t keep_lo = (key0 + 2 * e < total) ? 0x0000ffffu : 0u;
-          const uint32_t keep_hi = (key0 + 2 * e + 1 < total) ? 0xffff0000u : 0u;
-          stg[PER_T + i][e] &= (keep_lo | keep_hi);
-        }
-      }
-    }
+  // LDS: K tiles at [0, 2*TB_), V tiles at [2*TB_, 4*TB_) bytes
+  constexpr uint32_t TB_ = TEL * 2;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(smem)));
+  const uint16_t* ks[2] = {smem, smem + TEL};
+  const uint16_t* vs[2] = {smem + 2 * TEL, smem + 3 * TEL};
+
+  // ---- HBM -> LDS.  Wave w loads page w of a tile.  K: LDS chunk
+  // (page, cc, perm32(key)) holds dims 8cc..8cc+7 of the page's key; V: LDS
+  // chunk (page, h8, perm32(d-row)) holds slots 8*h8..8*h8+7 of that d-row.
+  // The lane offset inside the page is fixed; the page and the instruction's
+  // share of it go in the scalar offset.
+  const uint32_t kvo = static_cast<uint32_t>(perm32(lane & 15) * (2 * D) + (lane >> 4) * 16);
+  const uint32_t vvo = static_cast<uint32_t>(perm32(lane) * 32);
+  // page-table entry of this wave's page of tile kt (read one step ahead, so
+  // the load has landed when the page is used)
+  auto page_id = [&](int kt) -> int { return trow[min(kt * 4 + wave, last_page)]; };
+  auto page_off = [&](int phys) -> uint32_t {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(phys) * Hkv + g) * static_cast<uint32_t>(32 * D);
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* kl_s = smem + buf * S::BUF;
-    uint16_t* vl_s = kl_s + S::K_ELEMS;
+  auto issue_k = [&](int phys, int buf) {
+    const uint32_t so = page_off(phys);
+    const uint32_t dst = lds0 + buf * TB_ + wave * (PCH * 16);
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ci = threadIdx.x + 256 * i;
-      const int kl = ci / (D / 8);
-      const int ch = ci - kl * (D / 8);
-      *reinterpret_cast<u32x4*>(kl_s + kl * S::KPAD + ch * 8) = stg[i];
-    }
+    for (int i = 0; i < NI; ++i) dma16(krs, dst + i * 1024, kvo, so + i * 64);
+  };
+  auto issue_v = [&](int phys, int buf) {
+    const uint32_t so = page_off(phys);
+    const uint32_t dst = lds0 + (2 + buf) * TB_ + wave * (PCH * 16);
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ci = threadIdx.x + 256 * i;
-      const int pl = ci / (D * 2);
-      const int rem = ci - pl * (D * 2);
-      const int dd = rem >> 1;
-      const int h8 = rem & 1;
-      *reinterpret_cast<u32x4*>(vl_s + dd * S::VPAD + pl * 16 + h8 * 8) = stg[PER_T + i];
+    for (int i = 0; i < NI; ++i) dma16(vrs, dst + i * 1024, vvo, so + ((i * 64) % D) * 32 + ((i * 64) / D) * 16);
+  };
+  // zero the value slots >= total of this wave's page of tile kt (after its loads landed)
+  auto fix_v = [&](int kt, int buf) {
+    const int s0 = (kt * 4 + wave) * 16;
+    if (s0 + 16 <= total) return;
+    uint16_t* reg = smem + (2 + buf) * TEL + wave * PCH * 8;
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      const int q = r * 64 + lane;
+      const int slot = s0 + (q / D) * 8;
+      u32x4 w = *reinterpret_cast<u32x4*>(reg + q * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t keep_lo = (slot + 2 * e < total) ? 0x0000ffffu : 0u;
+        const uint32_t keep_hi = (slot + 2 * e + 1 < total) ? 0xffff0000u : 0u;
+        w[e] &= (keep_lo | keep_hi);
+      }
+      *reinterpret_cast<u32x4*>(reg + q * 8) = w;
     }
   };
 
-  f32x16 o[R][NDB];
-  float m_ref[R], m_seen[R], l_run[R];
+  // LDS read offsets (elements) of this lane's MFMA operands
+  const int kread = ((col >> 4) * PCH + half * 16 + (col & 15)) * 8;
+  const int vread = (half * D + col) * 8;
+
+  auto qk = [&](const uint16_t* kb, f32x16 (&s)[2]) {
+    const uint16_t* kr = kb + kread;
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    m_ref[j] = -INFINITY;              // set from the first sub-tile of the row-block
-    m_seen[j] = -INFINITY;
-  }
-  const int krow_l = perm32(col);
-  bool all_ok = true;
-#pragma unroll
-  for (int j = 0; j < R; ++j) all_ok = all_ok && rb_ok[j];
-  bool ovf = false;
-  int pass = 0;
-  __shared__ int redo;
-  // softmax of one 32-key sub-tile for row-block j: mask, row maximum,
-  // probabilities against the row's reference, row sum, bf16 B operands
-  auto softmax32 = [&](f32x16& sc, int j, int k0, bool msk, bf16x8* pf) {
-    if (msk) {
-      const int pos = c0 + t0 + rb_t[j] + col;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 16 * (i >> 3) + 8 * half + (i & 7);
-        if (key > pos) sc[i] = -INFINITY;
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kr + c * 256);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kr + 2 * PCH * 8 + c * 256);
+      if (c == 0) {
+        const f32x16 z = {};
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], z, 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[0], z, 0, 0, 0);
+      } else {
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[c], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[c], s[1], 0, 0, 0);
       }
     }
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
-    mx = fmaxf(mx, sc[15]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    if (pass == 0 && k0 == 0) m_ref[j] = mx;      // first sub-tile of every row-block
-    m_seen[j] = fmaxf(m_seen[j], mx);
-    ovf |= mx > m_ref[j] + 64.f;
-    const float mneg = -m_ref[j];
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], sl2, mneg));
-      lsum += p;
-      pf[i >> 3][i & 7] = static_cast<__bf16>(p);
-    }
-    l_run[j] += lsum;
   };
 
-  auto compute_tile = [&](const uint16_t* kl_s, const uint16_t* vl_s, int kt, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    if constexpr (R == 1) {
-      // both 32-key sub-tiles at once: two independent accumulator chains
-      const int qlo = c0 + t0 + rb_t[0];
-      bool act[2], msk[2];
+  f32x16 o[NDB];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int k0 = kt * KT + sub * 32;
-        act[sub] = MASKED ? (rb_ok[0] && k0 <= qlo + 31) : true;
-        msk[sub] = MASKED && k0 + 31 > qlo;
-      }
-      f32x16 sc[2];
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float l0 = 0.f, l1 = 0.f, mneg;
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+
+  // Two softmax elements i, i+1 (i even) of a 32-key sub-tile whose first key
+  // is k0: probabilities against the row reference, rounded to bf16 into the
+  // B operand pf (8 elements per 16-key half), row sum of the rounded values.
+  auto sm2 = [&](const f32x16& s, int i, int k0, bf16x8& pf, float& l, auto masked) {
+    float x0 = s[i], x1 = s[i + 1];
+    if constexpr (decltype(masked)::value) {
+      const int lim = qpos - k0 - 8 * half;     // key k0 + 16*(i/8) + 8*half + i%8 visible iff offset <= lim
+      if (16 * (i >> 3) + (i & 7) > lim) x0 = -INFINITY;
+      if (16 * (i >> 3) + (i & 7) + 1 > lim) x1 = -INFINITY;
+    }
+    const bf16x2 p = {static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(x0, sl2, mneg))),
+                      static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(x1, sl2, mneg)))};
+    l = __builtin_amdgcn_fdot2_f32_bf16(p, ones, l, false);
+    pf[i & 7] = p[0];
+    pf[(i & 7) + 1] = p[1];
+  };
+  auto kfrag = [&](const uint16_t* kb, int c, int sub) {
+    return *reinterpret_cast<const bf16x8*>(kb + kread + sub * 2 * PCH * 8 + c * 256);
+  };
+  auto vfrag = [&](const uint16_t* vb, int sub, int kb, int db) {
+    return *reinterpret_cast<const bf16x8*>(vb + vread + ((sub * 2 + kb) * PCH + db * 32) * 8);
+  };
+
+  // One tile of the pipeline: softmax and P.V of tile j (scores in cur, V in
+  // vb) with, when NEXT, the scores of tile j+1 (K in kb) into nxt.  The
+  // order is fixed by scheduling fences: the score products of tile j+1 carry
+  // the softmax of sub-tile 0, the first half of P.V carries sub-tile 1, and
+  // every operand read is issued one product ahead.
+  auto body = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint16_t* kb, const uint16_t* vb, int kbase,
+                  auto masked, auto next) {
+    constexpr bool NEXT = decltype(next)::value;
+    bf16x8 pf[2][2];
+    if constexpr (NEXT) {
+      bf16x8 ka0 = kfrag(kb, 0, 0), ka1 = kfrag(kb, 0, 1);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[sub][i] = 0.f;
-      const uint16_t* kr = kl_s + krow_l * S::KPAD + half * 8;
-      if (!MASKED || act[1]) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kr + c * 16);
-          const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(kr + 32 * S::KPAD + c * 16);
-          sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0][c], sc[0], 0, 0, 0);
-          sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[0][c], sc[1], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        bf16x8 kn0, kn1;
+        if (c + 1 < NC) {
+          kn0 = kfrag(kb, c + 1, 0);
+          kn1 = kfrag(kb, c + 1, 1);
         }
-      } else if (act[0]) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kr + c * 16);
-          sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0][c], sc[0], 0, 0, 0);
+        if (c == 0) {
+          const f32x16 z = {};
+          nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qf[0], z, 0, 0, 0);
+          nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf[0], z, 0, 0, 0);
+        } else {
+          nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qf[c], nxt[0], 0, 0, 0);
+          nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf[c], nxt[1], 0, 0, 0);
         }
-      }
-      bf16x8 pf[2][2];
+        // sub-tile 0 of tile j: 16 elements over NC steps
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-        if (!MASKED || act[sub]) softmax32(sc[sub], 0, kt * KT + sub * 32, msk[sub], pf[sub]);
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (MASKED && !act[sub]) continue;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-                vl_s + (db * 32 + krow_l) * S::VPAD + sub * 32 + kb * 16 + half * 8);
-            o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[sub][kb], o[0][db], 0, 0, 0);
-          }
+        for (int t = 0; t < 16 / NC; t += 2) {
+          const int i = c * (16 / NC) + t;
+          sm2(cur[0], i, kbase, pf[0][i >> 3], l0, masked);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        ka0 = kn0;
+        ka1 = kn1;
       }
     } else {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int k0 = kt * KT + sub * 32;
-        bool act[R];
-        bool msk[R];
+      for (int i = 0; i < 16; i += 2) sm2(cur[0], i, kbase, pf[0][i >> 3], l0, masked);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P.V: sub-tile 0 (carrying the softmax of sub-tile 1), then sub-tile 1;
+    // value operands are read two products ahead
+    constexpr int NU = 4 * NDB;
+    auto vfrag_u = [&](int u) { return vfrag(vb, u / (2 * NDB), (u / NDB) & 1, u % NDB); };
+    bf16x8 va = vfrag_u(0), vn = vfrag_u(1);
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-          const int qlo = c0 + t0 + rb_t[j];         // smallest query position of the row-block
-          act[j] = MASKED ? (rb_ok[j] && k0 <= qlo + 31) : true;
-          msk[j] = MASKED && k0 + 31 > qlo;
+    for (int u = 0; u < NU; ++u) {
+      const int sub = u / (2 * NDB), kk = (u / NDB) & 1, db = u % NDB;
+      bf16x8 vnn;
+      if (u + 2 < NU) vnn = vfrag_u(u + 2);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[sub][kk], o[db], 0, 0, 0);
+      if (u < 2 * NDB) {
+#pragma unroll
+        for (int t = 0; t < 16 / (2 * NDB); t += 2) {
+          const int i = u * (16 / (2 * NDB)) + t;
+          sm2(cur[1], i, kbase + 32, pf[1][i >> 3], l1, masked);
         }
-        f32x16 sc[R];
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[j][i] = 0.f;
-        const uint16_t* kr = kl_s + (sub * 32 + krow_l) * S::KPAD + half * 8;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + c * 16);
-#pragma unroll
-          for (int j = 0; j < R; ++j)
-            if (act[j]) sc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], sc[j], 0, 0, 0);
-        }
-        bf16x8 pf[R][2];
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-          if (act[j]) softmax32(sc[j], j, k0, msk[j], pf[j]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-                vl_s + (db * 32 + krow_l) * S::VPAD + sub * 32 + kb * 16 + half * 8);
-#pragma unroll
-            for (int j = 0; j < R; ++j)
-              if (act[j]) o[j][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][kb], o[j][db], 0, 0, 0);
-          }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      va = vn;
+      vn = vnn;
     }
   };
 
-  for (pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[j][db][i] = 0.f;
-      l_run[j] = 0.f;
+  // step j (P = j & 1): K(j) and V(j) sit in buffer P, K(j+1) in buffer 1-P;
+  // K(j+2) replaces K(j) and V(j+1) fills V buffer 1-P.  MODE 0: a tile wholly
+  // visible to every query of the workgroup, with a next tile; 1: any tile.
+  int pg_k = 0, pg_v = 0;                    // pages of K(j+2) and V(j+1) for step j
+  auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto parity, auto any) {
+    constexpr int P = decltype(parity)::value ? 1 : 0;
+    const bool has_next = j + 1 < ntk;
+    if (j + 2 < ntk) issue_k(pg_k, P);
+    if (has_next) issue_v(pg_v, 1 - P);
+    const int kbase = j * KT;
+    if constexpr (!decltype(any)::value) {
+      body(cur, nxt, ks[1 - P], vs[P], kbase, F_(), T_());
+    } else {
+      if (has_next) body(cur, nxt, ks[1 - P], vs[P], kbase, T_(), T_());
+      else body(cur, nxt, ks[1 - P], vs[P], kbase, T_(), F_());
     }
-    ovf = false;
-    load_tile(0);
-    store_tile(0);
+    if (j + 3 < ntk) pg_k = page_id(j + 3);
+    if (j + 2 < ntk) pg_v = page_id(j + 2);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (has_next) fix_v(j + 1, 1 - P);
     __syncthreads();
+  };
 
+  f32x16 sA[2], sB[2];
+  issue_k(page_id(0), 0);
+  issue_v(page_id(0), 0);
+  if (ntk > 1) issue_k(page_id(1), 1);
+  if (ntk > 2) pg_k = page_id(2);
+  if (ntk > 1) pg_v = page_id(1);
+  __builtin_amdgcn_s_waitcnt(0);
+  fix_v(0, 0);
+  __syncthreads();
+  qk(ks[0], sA);
+  {
+    // reference: maximum of the row's visible keys among keys 0..31
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 16 * (i >> 3) + 8 * half + (i & 7);
+      mx = fmaxf(mx, key <= qpos ? sA[0][i] : -INFINITY);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mneg = -(mx * sl2);
+  }
+  __syncthreads();                           // K(0) is read by every wave before K(2) replaces it
+  // leading tiles wholly visible to the whole workgroup (each with a next
+  // tile) in pairs, then the rest with masks
+  const int nfull = min((c0 + t0 + 1) / KT, ntk - 1);
+  int j = 0;
+  for (; j + 2 <= nfull; j += 2) {
+    step(j, sA, sB, F_(), F_());
+    step(j + 1, sB, sA, T_(), F_());
+  }
+  for (; j < ntk; j += 2) {
+    step(j, sA, sB, F_(), T_());
+    if (j + 1 < ntk) step(j + 1, sB, sA, T_(), T_());
+  }
+
+  // A row whose sum passed 2^64 (or is not finite) had a score far above its
+  // reference: find the exact row maxima (scores only) and run once more,
+  // one tile at a time, against them.
+  float l = l0 + l1;
+  float l_tot = l + __shfl_xor(l, 32);
+  if (__syncthreads_or(q_ok && !(l_tot <= 0x1p64f))) {
+    float m = -INFINITY;
     for (int kt = 0; kt < ntk; ++kt) {
-      const bool more = kt + 1 < ntk;
-      if (more) load_tile(kt + 1);
-      const uint16_t* kl_s = smem + (kt & 1) * S::BUF;
-      const uint16_t* vl_s = kl_s + S::K_ELEMS;
-      // tiles wholly at or below every row-block's smallest query position need
-      // neither masks nor activity checks
-      if (kt * KT + KT - 1 <= c0 + t0 && all_ok) {
-        compute_tile(kl_s, vl_s, kt, std::integral_constant<bool, false>());
-      } else {
-        compute_tile(kl_s, vl_s, kt, std::integral_constant<bool, true>());
-      }
-      if (more) store_tile((kt + 1) & 1);
+      issue_k(page_id(kt), 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      qk(ks[0], sA);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt * KT + sub * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
+          m = fmaxf(m, key <= qpos ? sA[sub][i] : -INFINITY);
+        }
       __syncthreads();
     }
-    // does any lane of the workgroup need a second pass?
-    if (threadIdx.x == 0) redo = 0;
-    __syncthreads();
-    if (__any(ovf) && lane == 0) redo = 1;
-    __syncthreads();
-    if (!redo) break;
+    m = fmaxf(m, __shfl_xor(m, 32));
+    mneg = -(m * sl2);
 #pragma unroll
-    for (int j = 0; j < R; ++j) m_ref[j] = m_seen[j];
-    __syncthreads();
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    l0 = 0.f;
+    l1 = 0.f;
+    for (int kt = 0; kt < ntk; ++kt) {
+      const int pid = page_id(kt);
+      issue_k(pid, 0);
+      issue_v(pid, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      fix_v(kt, 0);
+      __syncthreads();
+      qk(ks[0], sA);
+      body(sA, sB, ks[0], vs[0], kt * KT, T_(), F_());
+      __syncthreads();
+    }
+    l = l0 + l1;
+    l_tot = l + __shfl_xor(l, 32);
   }
 
+  const float inv = 1.f / l_tot;
+  if (q_ok) {
+    uint16_t* orow = static_cast<uint16_t*>(a.O) + b * a.o_s0 + static_cast<int64_t>(rb_h) * a.o_s1 +
+                     static_cast<int64_t>(r0 + t0 + rb_t + col) * a.o_s2;
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
-    const float inv = 1.f / l_tot;
-    if (rb_ok[j] && rb_t[j] + col < qn) {
-      uint16_t* orow = static_cast<uint16_t*>(a.O) + b * a.o_s0 + static_cast<int64_t>(rb_h[j]) * a.o_s1 +
-                       static_cast<int64_t>(r0 + t0 + rb_t[j] + col) * a.o_s2;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 w;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = pack_bf16x2(o[j][db][kb * 8 + 2 * e] * inv, o[j][db][kb * 8 + 2 * e + 1] * inv);
-          *reinterpret_cast<u32x4*>(orow + db * 32 + kb * 16 + half * 8) = w;
-        }
-    }
+        for (int e = 0; e < 8; ++e) w[e] = static_cast<__bf16>(o[db][kb * 8 + e] * inv);
+        *reinterpret_cast<bf16x8*>(orow + db * 32 + kb * 16 + half * 8) = w;
+      }
   }
+  zero_padding();
 }
 
 // Heads per workgroup (Gc, dividing G) and 32-token blocks per workgroup (TB)
-// with Gc * TB = 4 * R and TB >= GQA_PREFILL_MIN_TB (two 32-token blocks:
-// 64-token query tiles match the 64-key tiles, which keeps the diagonal's
-// masked work small): three row-blocks per wave when the group size allows,
-// else two, else one.
+// with Gc * TB = 4 (one row-block per wave) and TB >= 2: 64-token query tiles
+// match the 64-key tiles, which keeps the diagonal's masked work small.
 struct PrefillShape {
-  int Gc, TB, R;
+  int Gc, TB;
 };
 
-#ifndef GQA_PREFILL_MAX_R
-#define GQA_PREFILL_MAX_R 1
-#endif
-
-#ifndef GQA_PREFILL_MIN_TB
-#define GQA_PREFILL_MIN_TB 2
-#endif
-
 static PrefillShape prefill_shape(int G) {
-  for (int R = GQA_PREFILL_MAX_R; R >= 1; --R)
-    for (int Gc = G; Gc >= 1; --Gc)
-      if (G % Gc == 0 && (4 * R) % Gc == 0 && 4 * R / Gc >= GQA_PREFILL_MIN_TB) return {Gc, 4 * R / Gc, R};
-  return {1, 4, 1};
+  for (int Gc = 2; Gc >= 1; --Gc)
+    if (G % Gc == 0) return {Gc, 4 / Gc};
+  return {1, 4};
 }
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
@@ -478,17 +501,10 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   const int Tq = 32 * ps.TB;
   dim3 grid(a.Hkv * (G / ps.Gc), a.nseq, (a.n_rect + Tq - 1) / Tq);
   dim3 block(256);
-#define GQA_LAUNCH(DD, RR) hipLaunchKernelGGL((prefill_bf16_kernel<DD, RR>), grid, block, 0, s, a, ps.Gc, ps.TB)
-  if (a.d == 128) {
-    if (ps.R == 3) GQA_LAUNCH(128, 3);
-    else if (ps.R == 2) GQA_LAUNCH(128, 2);
-    else GQA_LAUNCH(128, 1);
-  } else {
-    if (ps.R == 3) GQA_LAUNCH(64, 3);
-    else if (ps.R == 2) GQA_LAUNCH(64, 2);
-    else GQA_LAUNCH(64, 1);
-  }
-#undef GQA_LAUNCH
+  if (a.d == 128)
+    hipLaunchKernelGGL((prefill_bf16_kernel<128>), grid, block, 0, s, a, ps.Gc, ps.TB);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<64>), grid, block, 0, s, a, ps.Gc, ps.TB);
   return hipGetLastError();
 }
 
