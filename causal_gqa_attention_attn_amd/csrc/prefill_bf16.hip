@@ -86,6 +86,22 @@ __device__ __forceinline__ void dma16(i32x4 r, uint32_t lds_addr, uint32_t voff,
       : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff));
 }
 
+// s_waitcnt immediate that waits for vector-memory count <= n only.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Scalar 32-bit load of base[byte_off/4], issued without a wait: the value
+// may be used only after sload_wait on it.
+__device__ __forceinline__ int sload(const int32_t* base, uint32_t byte_off) {
+  int v;
+  asm volatile("s_load_dword %0, %1, %2" : "=s"(v) : "s"(base), "s"(byte_off));
+  return v;
+}
+// Waits for outstanding scalar loads; the values pass through the statement
+// so that no use of them can be placed before it.
+__device__ __forceinline__ void sload_wait(int& a, int& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(a), "+s"(b));
+}
+
 }  // namespace
 
 template <int D>
@@ -205,9 +221,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   // share of it go in the scalar offset.
   const uint32_t kvo = static_cast<uint32_t>(perm32(lane & 15) * (2 * D) + (lane >> 4) * 16);
   const uint32_t vvo = static_cast<uint32_t>(perm32(lane) * 32);
-  // page-table entry of this wave's page of tile kt (read one step ahead, so
-  // the load has landed when the page is used)
-  auto page_id = [&](int kt) -> int { return trow[min(kt * 4 + wave, last_page)]; };
+  // page-table entry of this wave's page of tile kt: a scalar load whose
+  // wait is placed by the caller (sload_wait), so it never waits on the
+  // buffer-to-LDS loads in flight
+  auto page_id = [&](int kt) -> int {
+    return sload(trow, static_cast<uint32_t>(min(kt * 4 + wave, last_page)) * 4u);
+  };
   auto page_off = [&](int phys) -> uint32_t {
     return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(phys) * Hkv + g) * static_cast<uint32_t>(32 * D);
   };
@@ -298,16 +317,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     return *reinterpret_cast<const bf16x8*>(vb + vread + ((sub * 2 + kb) * PCH + db * 32) * 8);
   };
 
-  // One tile of the pipeline: softmax and P.V of tile j (scores in cur, V in
-  // vb) with, when NEXT, the scores of tile j+1 (K in kb) into nxt.  The
-  // order is fixed by scheduling fences: the score products of tile j+1 carry
-  // the softmax of sub-tile 0, the first half of P.V carries sub-tile 1, and
-  // every operand read is issued one product ahead.
-  auto body = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint16_t* kb, const uint16_t* vb, int kbase,
-                  auto masked, auto next) {
-    constexpr bool NEXT = decltype(next)::value;
-    bf16x8 pf[2][2];
-    if constexpr (NEXT) {
+  // One tile of the pipeline in two phases, their order fixed by scheduling
+  // fences.  Phase A: the score products of tile j+1 (when NEXT; K in kb,
+  // into nxt) carry the softmax of sub-tile 0 of tile j (scores in cur).
+  // Phase B: P.V of tile j (V in vb), whose first half carries the softmax of
+  // sub-tile 1.  Operand reads run one (K) or two (V) products ahead.
+  auto phase_a = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint16_t* kb, int kbase, bf16x8 (&pf)[2][2],
+                     auto masked, auto next) {
+    if constexpr (decltype(next)::value) {
       bf16x8 ka0 = kfrag(kb, 0, 0), ka1 = kfrag(kb, 0, 1);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -324,7 +341,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
           nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qf[c], nxt[0], 0, 0, 0);
           nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf[c], nxt[1], 0, 0, 0);
         }
-        // sub-tile 0 of tile j: 16 elements over NC steps
 #pragma unroll
         for (int t = 0; t < 16 / NC; t += 2) {
           const int i = c * (16 / NC) + t;
@@ -339,8 +355,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
       for (int i = 0; i < 16; i += 2) sm2(cur[0], i, kbase, pf[0][i >> 3], l0, masked);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // P.V: sub-tile 0 (carrying the softmax of sub-tile 1), then sub-tile 1;
-    // value operands are read two products ahead
+  };
+  auto phase_b = [&](f32x16 (&cur)[2], const uint16_t* vb, int kbase, bf16x8 (&pf)[2][2], auto masked) {
     constexpr int NU = 4 * NDB;
     auto vfrag_u = [&](int u) { return vfrag(vb, u / (2 * NDB), (u / NDB) & 1, u % NDB); };
     bf16x8 va = vfrag_u(0), vn = vfrag_u(1);
@@ -363,40 +379,65 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     }
   };
 
-  // step j (P = j & 1): K(j) and V(j) sit in buffer P, K(j+1) in buffer 1-P;
-  // K(j+2) replaces K(j) and V(j+1) fills V buffer 1-P.  MODE 0: a tile wholly
-  // visible to every query of the workgroup, with a next tile; 1: any tile.
-  int pg_k = 0, pg_v = 0;                    // pages of K(j+2) and V(j+1) for step j
+  // Wait until at most n of this wave's buffer-to-LDS loads are in flight
+  // (they complete in issue order); n is 0, NI or 2*NI.
+  auto wait_vm = [&](int n) {
+    if (n >= 2 * NI) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
+    else if (n >= NI) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+
+  // Step j (P = j & 1).  On entry K(j+1) sits in K buffer 1-P, V(j) is in
+  // flight or landed in V buffer P, K(j+2) is in flight to K buffer P, and
+  // the scores of tile j are in cur.  V(j+1) is issued at the start (into V
+  // buffer 1-P, free since P.V of tile j-1), K(j+3) after the mid-step
+  // barrier (into K buffer 1-P, free once every wave has scored tile j+1), so
+  // each load has about one and a half steps to land.  MODE any = false: a
+  // tile wholly visible to every query of the workgroup, with a next tile.
+  int pg_v = 0, pg_k = 0;                    // pages of V(j+1) and K(j+3) for step j
   auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto parity, auto any) {
     constexpr int P = decltype(parity)::value ? 1 : 0;
     const bool has_next = j + 1 < ntk;
-    if (j + 2 < ntk) issue_k(pg_k, P);
     if (has_next) issue_v(pg_v, 1 - P);
+    const int nv = page_id(j + 2), nk = page_id(j + 4);
     const int kbase = j * KT;
+    bf16x8 pf[2][2];
     if constexpr (!decltype(any)::value) {
-      body(cur, nxt, ks[1 - P], vs[P], kbase, F_(), T_());
+      phase_a(cur, nxt, ks[1 - P], kbase, pf, F_(), T_());
     } else {
-      if (has_next) body(cur, nxt, ks[1 - P], vs[P], kbase, T_(), T_());
-      else body(cur, nxt, ks[1 - P], vs[P], kbase, T_(), F_());
+      if (has_next) phase_a(cur, nxt, ks[1 - P], kbase, pf, T_(), T_());
+      else phase_a(cur, nxt, ks[1 - P], kbase, pf, T_(), F_());
     }
-    if (j + 3 < ntk) pg_k = page_id(j + 3);
-    if (j + 2 < ntk) pg_v = page_id(j + 2);
-    __builtin_amdgcn_s_waitcnt(0);
-    if (has_next) fix_v(j + 1, 1 - P);
+    // V(j) must have landed; K(j+2) and V(j+1) may still be in flight
+    wait_vm((j + 2 < ntk ? NI : 0) + (has_next ? NI : 0));
+    fix_v(j, P);
+    __syncthreads();
+    if (j + 3 < ntk) issue_k(pg_k, 1 - P);
+    if constexpr (!decltype(any)::value) phase_b(cur, vs[P], kbase, pf, F_());
+    else phase_b(cur, vs[P], kbase, pf, T_());
+    // K(j+2) must have landed; V(j+1) and K(j+3) may still be in flight
+    wait_vm((has_next ? NI : 0) + (j + 3 < ntk ? NI : 0));
+    pg_v = nv;
+    pg_k = nk;
+    sload_wait(pg_v, pg_k);
     __syncthreads();
   };
 
   f32x16 sA[2], sB[2];
-  issue_k(page_id(0), 0);
-  issue_v(page_id(0), 0);
-  if (ntk > 1) issue_k(page_id(1), 1);
-  if (ntk > 2) pg_k = page_id(2);
-  if (ntk > 1) pg_v = page_id(1);
-  __builtin_amdgcn_s_waitcnt(0);
-  fix_v(0, 0);
-  __syncthreads();
-  qk(ks[0], sA);
   {
+    int p0 = page_id(0), p1 = page_id(1);
+    sload_wait(p0, p1);
+    issue_k(p0, 0);
+    issue_v(p0, 0);
+    if (ntk > 1) issue_k(p1, 1);
+    pg_v = page_id(1);
+    int p2 = page_id(2);
+    pg_k = page_id(3);
+    sload_wait(pg_v, p2);
+    sload_wait(pg_k, p2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    qk(ks[0], sA);
     // reference: maximum of the row's visible keys among keys 0..31
     float mx = -INFINITY;
 #pragma unroll
@@ -406,8 +447,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     mneg = -(mx * sl2);
+    __syncthreads();                         // K(0) is read by every wave before K(2) replaces it
+    if (ntk > 2) issue_k(p2, 0);
   }
-  __syncthreads();                           // K(0) is read by every wave before K(2) replaces it
   // leading tiles wholly visible to the whole workgroup (each with a next
   // tile) in pairs, then the rest with masks
   const int nfull = min((c0 + t0 + 1) / KT, ntk - 1);
@@ -429,7 +471,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   if (__syncthreads_or(q_ok && !(l_tot <= 0x1p64f))) {
     float m = -INFINITY;
     for (int kt = 0; kt < ntk; ++kt) {
-      issue_k(page_id(kt), 0);
+      int pid = page_id(kt), unused = 0;
+      sload_wait(pid, unused);
+      issue_k(pid, 0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       qk(ks[0], sA);
@@ -451,14 +495,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     l0 = 0.f;
     l1 = 0.f;
     for (int kt = 0; kt < ntk; ++kt) {
-      const int pid = page_id(kt);
+      int pid = page_id(kt), unused = 0;
+      sload_wait(pid, unused);
       issue_k(pid, 0);
       issue_v(pid, 0);
       __builtin_amdgcn_s_waitcnt(0);
       fix_v(kt, 0);
       __syncthreads();
       qk(ks[0], sA);
-      body(sA, sB, ks[0], vs[0], kt * KT, T_(), F_());
+      bf16x8 pf[2][2];
+      phase_a(sA, sB, ks[0], kt * KT, pf, T_(), F_());
+      phase_b(sA, vs[0], kt * KT, pf, T_());
       __syncthreads();
     }
     l = l0 + l1;
