@@ -21,7 +21,8 @@ is one layer of the decode graph (one decode_bf16_kernel launch: append,
 split-T attention and split combine) against HBM.  ``cpu_baseline`` times the float64 oracle on a bounded sample of the
 same prefill (query rows spread over the sequence) on this host's cores.
 ``other_configs`` reports the other measured configurations on the same
-GPU, each timed with HIP events (median of 20 after 3 warm-ups):
+GPU, each timed with HIP events around 20 back-to-back calls (host-only
+truncates between calls), median and minimum of 5 such batches:
   * Llama-shaped prefill: B=8, n=2048, Hq=32, Hkv=8, d=128 (gqa_prefill);
   * serving decode: one gqa_decode_step of 64 sequences with lengths
     log-uniform in [512, 32768] on one layer (about 2.2 GB of K/V);
@@ -102,8 +103,12 @@ def cpu_baseline(inp, budget_s):
                       f"spread over the sequence, heaviest first), float64 numpy, {t_used:.1f} s"}
 
 
-def _median_ms(fn, before=None, iters=20, warm=3):
-    """Median and minimum event time of fn(); before() runs untimed each time."""
+def _median_ms(fn, before=None, iters=20, warm=3, reps=5):
+    """Per-call time of fn() when calls run back to back, as median and minimum
+    over ``reps`` batches of ``iters`` calls.  before() runs before every call;
+    it is host-only work (a truncate), so the GPU stays busy and the host
+    preparation of one call overlaps the kernels of the previous one, as in a
+    serving loop."""
     import torch
     for _ in range(warm):
         if before:
@@ -111,15 +116,16 @@ def _median_ms(fn, before=None, iters=20, warm=3):
         fn()
     torch.cuda.synchronize()
     ts = []
-    for _ in range(iters):
-        if before:
-            before()
+    for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        fn()
+        for _ in range(iters):
+            if before:
+                before()
+            fn()
         b.record()
         torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
+        ts.append(a.elapsed_time(b) / iters)
     ts.sort()
     return ts[len(ts) // 2], ts[0]
 

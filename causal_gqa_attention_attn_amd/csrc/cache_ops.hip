@@ -92,10 +92,112 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+// bfloat16 caches: the same writes in 16-byte units.  grid as above.
+//  * keys: a thread takes 8 dims of a slot and the 8 dims they pair with
+//    (i and i + D/2), rotates them in float32 exactly as the scalar path does
+//    and writes both 16-byte runs;
+//  * values: the page's rows are staged in LDS, then each thread writes 8
+//    consecutive slots of one d-row of the d-major page; a run that the call
+//    only partly covers keeps the slots it does not cover.
+template <int D>
+__global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
+  constexpr int PAIRS = D / 16;                 // 8-dim runs per half row
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kPage][D + 8];
+  const int b = blockIdx.z;
+  const int g = blockIdx.y;
+  const int nb = a.meta.count[b];
+  if (nb == 0) return;
+  const int seq = a.meta.seq[b];
+  const int c0 = a.meta.start[b];
+  const int r0 = a.meta.row0[b];
+  const int lp = c0 / kPage + static_cast<int>(blockIdx.x);
+  const int slot_lo = max(c0, lp * kPage);
+  const int slot_hi = min(c0 + nb, lp * kPage + kPage);
+  if (slot_lo >= slot_hi) return;
+  const int64_t phys = a.table[static_cast<int64_t>(seq) * a.table_w + lp];
+  uint16_t* kp = static_cast<uint16_t*>(a.k_pool) + (phys * a.Hkv + g) * (kPage * D);
+  uint16_t* vp = static_cast<uint16_t*>(a.v_pool) + (phys * a.Hkv + g) * (D * kPage);
+  const uint16_t* kin = static_cast<const uint16_t*>(a.K) + b * a.k_s0 + g * a.k_s1;
+  const uint16_t* vin = static_cast<const uint16_t*>(a.V) + b * a.v_s0 + g * a.v_s1;
+  const int t = threadIdx.x;
+
+  // keys
+  if (t < kPage * PAIRS) {
+    const int si = t / PAIRS;
+    const int p = t - si * PAIRS;
+    const int slot = lp * kPage + si;
+    if (slot >= slot_lo && slot < slot_hi) {
+      const uint16_t* row = kin + static_cast<int64_t>(r0 + slot - c0) * a.k_s2;
+      const u32x4 wlo = *reinterpret_cast<const u32x4*>(row + 8 * p);
+      const u32x4 whi = *reinterpret_cast<const u32x4*>(row + D / 2 + 8 * p);
+      u32x4 olo = wlo, ohi = whi;
+      if (a.rope) {
+        const float* rr = a.rope + (static_cast<int64_t>(slot) * (D / 2) + 8 * p) * 2;
+        f32x4 cs[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cs[q] = *reinterpret_cast<const f32x4*>(rr + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x[2], y[2], xo[2], yo[2];
+          x[0] = __uint_as_float(wlo[e] << 16);
+          x[1] = __uint_as_float(wlo[e] & 0xffff0000u);
+          y[0] = __uint_as_float(whi[e] << 16);
+          y[1] = __uint_as_float(whi[e] & 0xffff0000u);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int i = 2 * e + h;            // pair 8p + i: (cos, sin) at rr[2i], rr[2i + 1]
+            const float c = cs[i / 2][(i % 2) * 2];
+            const float sn = cs[i / 2][(i % 2) * 2 + 1];
+            rotate_pair(x[h], y[h], c, sn, xo[h], yo[h]);
+          }
+          olo[e] = pack_bf16x2(xo[0], xo[1]);
+          ohi[e] = pack_bf16x2(yo[0], yo[1]);
+        }
+      }
+      uint16_t* krow = kp + (slot % kPage) * D;
+      *reinterpret_cast<u32x4*>(krow + 8 * p) = olo;
+      *reinterpret_cast<u32x4*>(krow + D / 2 + 8 * p) = ohi;
+    }
+  }
+  // values: rows of the page into LDS (slots the call does not write stay unread)
+  for (int e = t; e < kPage * (D / 8); e += 256) {
+    const int si = e / (D / 8);
+    const int ch = e - si * (D / 8);
+    const int slot = lp * kPage + si;
+    if (slot >= slot_lo && slot < slot_hi)
+      *reinterpret_cast<u32x4*>(&vt[si][ch * 8]) =
+          *reinterpret_cast<const u32x4*>(vin + static_cast<int64_t>(r0 + slot - c0) * a.v_s2 + ch * 8);
+  }
+  __syncthreads();
+  for (int e = t; e < D * 2; e += 256) {
+    const int dr = e >> 1;
+    const int h8 = e & 1;
+    const int s0 = lp * kPage + h8 * 8;
+    if (s0 + 8 <= slot_lo || s0 >= slot_hi) continue;
+    uint16_t* dst = vp + dr * kPage + h8 * 8;
+    u32x4 w;
+    const bool whole = s0 >= slot_lo && s0 + 8 <= slot_hi;
+    if (!whole) w = *reinterpret_cast<const u32x4*>(dst);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t lo = w[q] & 0xffffu, hi = w[q] >> 16;
+      const int sa = s0 + 2 * q, sb = sa + 1;
+      if (whole || (sa >= slot_lo && sa < slot_hi)) lo = vt[h8 * 8 + 2 * q][dr];
+      if (whole || (sb >= slot_lo && sb < slot_hi)) hi = vt[h8 * 8 + 2 * q + 1][dr];
+      w[q] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(dst) = w;
+  }
+}
+
 hipError_t launch_append(const AppendArgs& a, int dtype, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, a.Hkv, a.nseq);
   if (dtype == 0)
     hipLaunchKernelGGL(append_kernel<float>, grid, dim3(256), 0, s, a);
+  else if (a.d == 128)
+    hipLaunchKernelGGL(append_bf16_kernel<128>, grid, dim3(256), 0, s, a);
+  else if (a.d == 64)
+    hipLaunchKernelGGL(append_bf16_kernel<64>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(append_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

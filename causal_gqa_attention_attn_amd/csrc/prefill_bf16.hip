@@ -54,6 +54,14 @@ namespace gqa {
 namespace {
 
 constexpr int KT = 64;                 // keys per tile (four 16-slot pages)
+#ifndef GQA_PF_LAK
+#define GQA_PF_LAK 2
+#endif
+#ifndef GQA_PF_LAV
+#define GQA_PF_LAV 3
+#endif
+constexpr int LAK = GQA_PF_LAK;        // score products a key operand read runs ahead
+constexpr int LAV = GQA_PF_LAV;        // P.V products a value operand read runs ahead
 
 // Swaps bits 2 and 3 (an involution).  MFMA row r is fed key (or d-row)
 // perm32(r), which keeps the accumulator of rows 8*(i/4) + 4*half + i%4 equal
@@ -84,6 +92,13 @@ __device__ __forceinline__ void dma16(i32x4 r, uint32_t lds_addr, uint32_t voff,
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff));
+}
+
+// Keeps the computation of x at this point of the program: passes the value
+// through an empty statement the compiler cannot move or look into.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
 // s_waitcnt immediate that waits for vector-memory count <= n only.
@@ -164,41 +179,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   const bool q_ok = rb_t + col < qn;
   const int qpos = c0 + t0 + rb_t + col;
 
-  // rotated queries as B operands: lane holds dims 16c + 8*half + 0..7 of its query
+  // rotated queries as B operands: lane holds dims 16c + 8*half + 0..7 of its
+  // query (loaded once the first key/value tiles are in flight)
   bf16x8 qf[NC];
-  {
-    float x[NC][8];
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.q_s0 + static_cast<int64_t>(rb_h) * a.q_s1 +
-                           static_cast<int64_t>(r0 + t0 + rb_t + col) * a.q_s2;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (q_ok) w = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[c][2 * e] = __uint_as_float(w[e] << 16);
-        x[c][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-      }
-    }
-    if (a.rope && q_ok) {
-      const float* rrow = a.rope + static_cast<int64_t>(qpos) * D;    // (D/2) (cos, sin) pairs
-#pragma unroll
-      for (int c = 0; c < NC / 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = c * 16 + half * 8 + e;
-          float lo, hi;
-          rotate_pair(x[c][e], x[c + NC / 2][e], rrow[2 * i], rrow[2 * i + 1], lo, hi);
-          x[c][e] = lo;
-          x[c + NC / 2][e] = hi;
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[c][e] = static_cast<__bf16>(x[c][e]);
-  }
-
   const int kv_end = c0 + t0 + qn;            // keys [0, kv_end) can be visible
   const int ntk = (kv_end + KT - 1) / KT;
   const int last_page = (total - 1) >> 4;
@@ -325,30 +308,34 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   auto phase_a = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint16_t* kb, int kbase, bf16x8 (&pf)[2][2],
                      auto masked, auto next) {
     if constexpr (decltype(next)::value) {
-      bf16x8 ka0 = kfrag(kb, 0, 0), ka1 = kfrag(kb, 0, 1);
+      bf16x8 kq[NC][2];
+#pragma unroll
+      for (int c = 0; c < LAK && c < NC; ++c) {
+        kq[c][0] = kfrag(kb, c, 0);
+        kq[c][1] = kfrag(kb, c, 1);
+      }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        bf16x8 kn0, kn1;
-        if (c + 1 < NC) {
-          kn0 = kfrag(kb, c + 1, 0);
-          kn1 = kfrag(kb, c + 1, 1);
+        if (c + LAK < NC) {
+          kq[c + LAK][0] = kfrag(kb, c + LAK, 0);
+          kq[c + LAK][1] = kfrag(kb, c + LAK, 1);
         }
         if (c == 0) {
           const f32x16 z = {};
-          nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qf[0], z, 0, 0, 0);
-          nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf[0], z, 0, 0, 0);
+          nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[0][0], qf[0], z, 0, 0, 0);
+          nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[0][1], qf[0], z, 0, 0, 0);
         } else {
-          nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qf[c], nxt[0], 0, 0, 0);
-          nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf[c], nxt[1], 0, 0, 0);
+          nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[c][0], qf[c], nxt[0], 0, 0, 0);
+          nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[c][1], qf[c], nxt[1], 0, 0, 0);
         }
 #pragma unroll
         for (int t = 0; t < 16 / NC; t += 2) {
           const int i = c * (16 / NC) + t;
           sm2(cur[0], i, kbase, pf[0][i >> 3], l0, masked);
         }
+        pin(pf[0][(c * (16 / NC)) >> 3]);
+        pin(l0);
         __builtin_amdgcn_sched_barrier(0);
-        ka0 = kn0;
-        ka1 = kn1;
       }
     } else {
 #pragma unroll
@@ -359,23 +346,24 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   auto phase_b = [&](f32x16 (&cur)[2], const uint16_t* vb, int kbase, bf16x8 (&pf)[2][2], auto masked) {
     constexpr int NU = 4 * NDB;
     auto vfrag_u = [&](int u) { return vfrag(vb, u / (2 * NDB), (u / NDB) & 1, u % NDB); };
-    bf16x8 va = vfrag_u(0), vn = vfrag_u(1);
+    bf16x8 vq[NU];
+#pragma unroll
+    for (int u = 0; u < LAV && u < NU; ++u) vq[u] = vfrag_u(u);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int sub = u / (2 * NDB), kk = (u / NDB) & 1, db = u % NDB;
-      bf16x8 vnn;
-      if (u + 2 < NU) vnn = vfrag_u(u + 2);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[sub][kk], o[db], 0, 0, 0);
+      if (u + LAV < NU) vq[u + LAV] = vfrag_u(u + LAV);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[u], pf[sub][kk], o[db], 0, 0, 0);
       if (u < 2 * NDB) {
 #pragma unroll
         for (int t = 0; t < 16 / (2 * NDB); t += 2) {
           const int i = u * (16 / (2 * NDB)) + t;
           sm2(cur[1], i, kbase + 32, pf[1][i >> 3], l1, masked);
         }
+        pin(pf[1][(u * (16 / (2 * NDB))) >> 3]);
+        pin(l1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      va = vn;
-      vn = vnn;
     }
   };
 
@@ -433,6 +421,38 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     pg_v = page_id(1);
     int p2 = page_id(2);
     pg_k = page_id(3);
+    {
+      float x[NC][8];
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.q_s0 + static_cast<int64_t>(rb_h) * a.q_s1 +
+                             static_cast<int64_t>(r0 + t0 + rb_t + col) * a.q_s2;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (q_ok) w = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[c][2 * e] = __uint_as_float(w[e] << 16);
+          x[c][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      }
+      if (a.rope && q_ok) {
+        const float* rrow = a.rope + static_cast<int64_t>(qpos) * D;    // (D/2) (cos, sin) pairs
+#pragma unroll
+        for (int c = 0; c < NC / 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = c * 16 + half * 8 + e;
+            float lo, hi;
+            rotate_pair(x[c][e], x[c + NC / 2][e], rrow[2 * i], rrow[2 * i + 1], lo, hi);
+            x[c][e] = lo;
+            x[c + NC / 2][e] = hi;
+          }
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[c][e] = static_cast<__bf16>(x[c][e]);
+    }
     sload_wait(pg_v, p2);
     sload_wait(pg_k, p2);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
