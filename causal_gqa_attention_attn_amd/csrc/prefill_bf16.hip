@@ -422,28 +422,40 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     int p2 = page_id(2);
     pg_k = page_id(3);
     {
-      float x[NC][8];
+      // every lane loads a valid row (padding lanes reuse the last valid one
+      // and are zeroed), so all query and rotation-table loads issue together
+      const int tq = min(rb_t + col, qn - 1);
       const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.q_s0 + static_cast<int64_t>(rb_h) * a.q_s1 +
-                             static_cast<int64_t>(r0 + t0 + rb_t + col) * a.q_s2;
+                             static_cast<int64_t>(r0 + t0 + tq) * a.q_s2;
+      u32x4 w[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (q_ok) w = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
+      for (int c = 0; c < NC; ++c) w[c] = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
+      f32x4 cs[NC / 2][4];                   // (cos, sin) of pairs 16c + 8*half + 0..7
+      if (a.rope) {
+        const float* rrow = a.rope + static_cast<int64_t>(c0 + t0 + tq) * D;
+#pragma unroll
+        for (int c = 0; c < NC / 2; ++c)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            cs[c][q4] = *reinterpret_cast<const f32x4*>(rrow + 2 * (c * 16 + half * 8) + 4 * q4);
+      }
+      float x[NC][8];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[c][2 * e] = __uint_as_float(w[e] << 16);
-          x[c][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+          const uint32_t v = q_ok ? w[c][e] : 0u;
+          x[c][2 * e] = __uint_as_float(v << 16);
+          x[c][2 * e + 1] = __uint_as_float(v & 0xffff0000u);
         }
-      }
-      if (a.rope && q_ok) {
-        const float* rrow = a.rope + static_cast<int64_t>(qpos) * D;    // (D/2) (cos, sin) pairs
+      if (a.rope) {
 #pragma unroll
         for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int i = c * 16 + half * 8 + e;
             float lo, hi;
-            rotate_pair(x[c][e], x[c + NC / 2][e], rrow[2 * i], rrow[2 * i + 1], lo, hi);
+            rotate_pair(x[c][e], x[c + NC / 2][e], cs[c][e / 2][(e % 2) * 2], cs[c][e / 2][(e % 2) * 2 + 1], lo,
+                        hi);
             x[c][e] = lo;
             x[c + NC / 2][e] = hi;
           }
