@@ -508,3 +508,61 @@ def test_decode_many_splits(T):
         r = ref.decode(0, [0], as_f32(st.q), [T])
         compare_rows(o, r, torch.bfloat16)
     cache.close()
+
+
+# ------------------------------------------------------------------ stale cache memory
+
+def _poison_stale(pair, seq, layers):
+    """NaN into every slot of the sequence's pages at or past its length."""
+    lib = pair.lib
+    pages = lib.gqa_cache_page_table(pair.gpu.handle, seq)
+    kv, vv = pair.gpu.k_view(), pair.gpu.v_view()
+    for l in layers:
+        n = lib.gqa_cache_length(pair.gpu.handle, seq, l)
+        for lp, ph in enumerate(pages):
+            lo = max(n - lp * 16, 0)
+            if lo < 16:
+                kv[l, ph, :, lo:, :] = float("nan")
+                vv[l, ph, :, :, lo:] = float("nan")
+
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(128, 32, 8), (64, 8, 2)])
+def test_poisoned_cache_memory_never_reaches_outputs(d, Hq, Hkv):
+    """Stale and never-written cache slots may hold any bits (NaN here): slots
+    past a sequence's length, in its last partly written page, and slots a
+    truncate leaves behind.  None of them may reach a valid output."""
+    say(f"case: NaN-filled pools, ragged prefill, decode, truncate + re-prefill; d={d} Hq={Hq} Hkv={Hkv}")
+    lens = [37, 100, 1, 66]
+    B = len(lens)
+    n = max(lens)
+    shape = W.AttnShape(B=B, n=n, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4)
+    inp = W.prefill_inputs(shape, 4242, lengths=lens)
+    pair = Pair(1, Hkv, d, 64, B, 16, torch.bfloat16, 1e4, free_order=W.page_order(64, 9))
+    pair.gpu.k_pool.fill_(float("nan"))
+    pair.gpu.v_pool.fill_(float("nan"))
+    ids = list(range(B))
+    O, ref = pair.prefill(0, ids, inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+    valid = inp.mask.numpy().astype(bool)[:, None, :].repeat(Hq, 1)
+    compare_rows(O, ref, torch.bfloat16, rows_mask=valid)
+    for step in range(3):
+        o, r = pair.step_fused(0, ids, W.decode_step_inputs(shape, 4242, step))
+        compare_rows(o, r, torch.bfloat16)
+    pair.check_cache(ids)
+    # truncate inside a page, poison what it left behind, re-prefill the suffix
+    ms = [20, 51, 1, 64]
+    for s, m in zip(ids, ms):
+        pair.truncate(s, m)
+        _poison_stale(pair, s, [0])
+    torch.cuda.synchronize()
+    sl = [L + 3 - m for L, m in zip(lens, ms)]
+    suffix = W.prefill_inputs(W.AttnShape(B=B, n=max(sl), Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4),
+                              4343, lengths=sl, start=ms)
+    O, ref = pair.prefill(0, ids, suffix.Q, suffix.K, suffix.V, suffix.mask, suffix.positions)
+    valid = suffix.mask.numpy().astype(bool)[:, None, :].repeat(Hq, 1)
+    compare_rows(O, ref, torch.bfloat16, rows_mask=valid)
+    for s in ids:
+        _poison_stale(pair, s, [0])
+    torch.cuda.synchronize()
+    o, r = pair.step_fused(0, ids, W.decode_step_inputs(shape, 4343, 0))
+    compare_rows(o, r, torch.bfloat16)
+    pair.check_cache(ids)
