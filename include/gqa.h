@@ -74,6 +74,9 @@ typedef struct gqa_tensor {
  *  num_kv_heads      Hkv.   head_dim: d, 64 or 128 for bf16, 1..128 for f32.
  *  page_size         tokens per page; 16 is the only supported value.
  *  num_pages         physical pages in the pool (a page serves all layers).
+ *                    For bf16 one layer of a pool (num_pages*Hkv*16*d*2
+ *                    bytes) must stay below 4 GiB: the kernels address a
+ *                    layer with 32-bit byte offsets (GQA_ERR_UNSUPPORTED).
  *  max_seqs          sequence ids are 0..max_seqs-1.
  *  max_pages_per_seq block-table width.
  *  dtype             storage dtype of the cache and of all Q/K/V/O tensors.

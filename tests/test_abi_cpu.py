@@ -72,6 +72,15 @@ def test_config_checks():
     assert lib.STATUS[st] == "UNSUPPORTED"
     st, _ = _cache(lib, dtype=7)
     assert lib.STATUS[st] == "DTYPE"
+    # one bf16 layer of a pool must stay below 4 GiB (32 KiB per page at Hkv=8, d=128)
+    st, _ = _cache(lib, num_kv_heads=8, head_dim=128, num_pages=1 << 17)
+    assert lib.STATUS[st] == "UNSUPPORTED"
+    st, h = _cache(lib, num_kv_heads=8, head_dim=128, num_pages=(1 << 17) - 1)
+    assert st == 0
+    lib.gqa_cache_destroy(h)
+    st, h = _cache(lib, num_kv_heads=8, head_dim=128, num_pages=1 << 17, dtype=lib.F32)
+    assert st == 0, "the limit is on bf16 pools only"
+    lib.gqa_cache_destroy(h)
     st, h = _cache(lib)
     assert st == 0
     lib.gqa_cache_check(h)
