@@ -566,3 +566,22 @@ def test_poisoned_cache_memory_never_reaches_outputs(d, Hq, Hkv):
     o, r = pair.step_fused(0, ids, W.decode_step_inputs(shape, 4343, 0))
     compare_rows(o, r, torch.bfloat16)
     pair.check_cache(ids)
+
+
+@pytest.mark.parametrize("scale", [4.0, 8.0])
+def test_large_logits_bf16(scale):
+    """Queries and keys scaled up (raw scores 16x and 64x those of N(0,1) inputs):
+    the softmax must stay within the bf16 tolerance, so the kernel may not round
+    anything that multiplies with the score's magnitude (such as a query scaled
+    by the softmax factor before its bf16 rounding)."""
+    say(f"case: bf16 prefill with Q, K scaled by {scale}")
+    shape = W.AttnShape(B=2, n=300, Hq=16, Hkv=4, d=128, dtype=torch.bfloat16, theta=1e4)
+    inp = W.prefill_inputs(shape, 777, lengths=[300, 171])
+    Q = (inp.Q.float() * scale).to(torch.bfloat16)
+    K = (inp.K.float() * scale).to(torch.bfloat16)
+    pair = Pair(1, 4, 128, 64, 2, 24, torch.bfloat16, 1e4)
+    O, ref = pair.prefill(0, [0, 1], Q, K, inp.V, inp.mask, inp.positions)
+    valid = inp.mask.numpy().astype(bool)[:, None, :].repeat(16, 1)
+    compare_rows(O, ref, torch.bfloat16, rows_mask=valid)
+    o, r = pair.step_fused(0, [0, 1], W.decode_step_inputs(shape, 777, 0))
+    compare_rows(o, r, torch.bfloat16)
