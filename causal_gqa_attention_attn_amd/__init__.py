@@ -34,6 +34,7 @@ STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "MASK", -5: "POSITIO
 EXPORTS = ["gqa_cache_buffer_sizes", "gqa_cache_create", "gqa_cache_destroy", "kv_cache_append",
            "gqa_prefill", "gqa_attention", "gqa_decode", "gqa_decode_step", "kv_cache_truncate", "kv_cache_remap", "gqa_cache_length",
            "gqa_cache_page_table", "gqa_cache_free_pages", "gqa_cache_check", "gqa_workspace_size",
+           "gqa_attention_workspace_size",
            "gqa_last_error"]
 
 
@@ -80,6 +81,7 @@ _sig = {
     "gqa_cache_free_pages": [_P, _I32P],
     "gqa_cache_check": [_P],
     "gqa_workspace_size": [_P, ctypes.c_int32, ctypes.c_int32],
+    "gqa_attention_workspace_size": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
     "gqa_last_error": [],
 }
 for _name, _args in _sig.items():
@@ -87,6 +89,7 @@ for _name, _args in _sig.items():
     _fn.argtypes = _args
     _fn.restype = ctypes.c_int32
 _lib.gqa_workspace_size.restype = ctypes.c_size_t
+_lib.gqa_attention_workspace_size.restype = ctypes.c_size_t
 _lib.gqa_last_error.restype = ctypes.c_char_p
 
 
@@ -253,6 +256,10 @@ def gqa_cache_check(handle):
 
 def gqa_workspace_size(handle, B, Hq) -> int:
     return int(_lib.gqa_workspace_size(handle, B, Hq))
+
+
+def gqa_attention_workspace_size(handle, B, Hq, n) -> int:
+    return int(_lib.gqa_attention_workspace_size(handle, B, Hq, n))
 
 
 def gqa_last_error() -> str:

@@ -291,6 +291,17 @@ gqa_status launch_append_all(gqa_cache* c, int32_t layer, int32_t B, const int32
 }
 
 
+// Short query runs (at most GQA_MAX_CHUNK_TOKENS rectangular rows) of a bf16
+// cache go to the split-T kernel when the caller passes a workspace.
+bool use_split(const gqa_cache* c, int64_t n, const void* workspace) {
+  return c->cfg.dtype == GQA_BF16 && n >= 1 && n <= GQA_MAX_CHUNK_TOKENS && workspace != nullptr;
+}
+gqa_status check_split_workspace(const gqa_cache* c, int32_t B, int64_t Hq, int64_t n, const int32_t* start,
+                                 const int32_t* count, void* workspace, size_t ws_bytes);
+gqa_status attend_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* Q,
+                        const gqa_tensor* O, int64_t n, const int32_t* start, const int32_t* count,
+                        const int32_t* row0, void* workspace, size_t ws_bytes, hipStream_t s);
+
 // Causal attention of each row's valid queries (positions start[b].., count[b]
 // of them, from rectangular row row0[b]) against slots [0, position] of the
 // layer; total[b] = written length of the sequence in that layer.
@@ -433,8 +444,6 @@ GQA_EXPORT gqa_status gqa_prefill(gqa_cache* c, int32_t layer, int32_t B, const 
                                   const gqa_tensor* Q, const gqa_tensor* K, const gqa_tensor* V,
                                   const uint8_t* valid_mask, const int32_t* positions, const gqa_tensor* O,
                                   void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!c) return fail(GQA_ERR_ARG, "cache is null");
   const gqa_cache_config& cf = c->cfg;
   if (layer < 0 || layer >= cf.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
@@ -451,6 +460,11 @@ GQA_EXPORT gqa_status gqa_prefill(gqa_cache* c, int32_t layer, int32_t B, const 
   AppendPlan plan;
   st = plan_append(c, layer, B, seq_ids, K, V, valid_mask, positions, &plan);
   if (st != GQA_OK) return st;
+  const bool split = use_split(c, n, workspace);
+  if (split) {
+    st = check_split_workspace(c, B, Hq, n, plan.start.data(), plan.count.data(), workspace, ws_bytes);
+    if (st != GQA_OK) return st;
+  }
   commit_append(c, layer, B, seq_ids, plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = sync_metadata(c, s);
@@ -458,6 +472,9 @@ GQA_EXPORT gqa_status gqa_prefill(gqa_cache* c, int32_t layer, int32_t B, const 
   st = launch_append_all(c, layer, B, seq_ids, K, V, plan, s);
   if (st != GQA_OK) return st;
   if (n == 0) return GQA_OK;
+  if (split)
+    return attend_split(c, layer, B, seq_ids, Q, O, n, plan.start.data(), plan.count.data(), plan.row0.data(),
+                        workspace, ws_bytes, s);
   std::vector<int32_t> totals(B);
   for (int b = 0; b < B; ++b) totals[b] = plan.start[b] + plan.count[b];
   return launch_attention(c, layer, B, seq_ids, Q, O, n, plan.start.data(), plan.count.data(), plan.row0.data(),
@@ -467,8 +484,6 @@ GQA_EXPORT gqa_status gqa_prefill(gqa_cache* c, int32_t layer, int32_t B, const 
 GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
                                     const gqa_tensor* Q, const uint8_t* valid_mask, const int32_t* positions,
                                     const gqa_tensor* O, void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!c) return fail(GQA_ERR_ARG, "cache is null");
   const gqa_cache_config& cf = c->cfg;
   if (layer < 0 || layer >= cf.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
@@ -503,6 +518,12 @@ GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, cons
     totals[b] = have;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_split(c, n, workspace)) {
+    st = check_split_workspace(c, B, Hq, n, start.data(), count.data(), workspace, ws_bytes);
+    if (st != GQA_OK) return st;
+    return attend_split(c, layer, B, seq_ids, Q, O, n, start.data(), count.data(), row0.data(), workspace, ws_bytes,
+                        s);
+  }
   st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
   if (n == 0) return GQA_OK;
@@ -513,27 +534,33 @@ GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, cons
 
 namespace {
 
-struct WsLayout {
-  int64_t max_splits, part_floats, hdr_floats, flags;
-  size_t bytes;
+// Workspace of the split-T kernel, cut into slots of one (split, kv head x
+// column chunk) each: a ready-flag row of kDecodeMergers int32, 16 split o rows
+// of d float32 and 16 (m, l) headers.  The cut depends only on the workspace's
+// size and d, never on a call's shape, so calls of any B, Hq or chunk length
+// can share one workspace: the flags sit first and every call leaves them zero.
+struct WsView {
+  int32_t* flags = nullptr;
+  float* part_o = nullptr;
+  float* part_h = nullptr;
+  int64_t slots = 0;
 };
 
-// Workspace: split o rows [split][kv head x head chunk][16][d] float32, then
-// (m, l) headers [split][kv head x head chunk][16][2] float32, then int32 ready
-// flags, kDecodeMergers per (split, kv head x chunk).
-// Whatever the lengths, a call makes at most ceil(target / (Hkv * chunks)) + B
-// splits (see decode_splits).
-WsLayout ws_layout(const gqa_cache* c, int64_t B, int64_t Hq) {
-  WsLayout w;
-  const int64_t chunks = ceil_div(std::max<int64_t>(1, Hq / c->cfg.num_kv_heads), 16);
-  const int64_t ys = c->cfg.num_kv_heads * chunks;
-  w.max_splits = ceil_div(kDecodeTargetBlocks, ys) + B;
-  w.part_floats = w.max_splits * ys * 16 * static_cast<int64_t>(c->cfg.head_dim);
-  w.hdr_floats = w.max_splits * ys * 16 * 2;
-  w.flags = w.max_splits * ys * gqa::kDecodeMergers;
-  w.bytes = static_cast<size_t>((w.part_floats + w.hdr_floats + w.flags) * 4);
-  return w;
+int64_t ws_slot_bytes(int64_t d) { return (16 * d + 16 * 2 + gqa::kDecodeMergers) * 4; }
+
+WsView ws_view(void* ws, size_t bytes, int64_t d) {
+  WsView v;
+  if (!ws || bytes < 256) return v;
+  v.slots = static_cast<int64_t>((bytes - 256) / ws_slot_bytes(d));
+  v.flags = static_cast<int32_t*>(ws);
+  const int64_t flag_bytes = ceil_div(v.slots * gqa::kDecodeMergers * 4, 256) * 256;
+  v.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + flag_bytes);
+  v.part_h = v.part_o + v.slots * 16 * d;
+  return v;
 }
+
+// (kv head x column chunk) rows of the grid for ncol (token, head) columns
+int64_t split_ys(const gqa_cache* c, int64_t ncol) { return c->cfg.num_kv_heads * ceil_div(ncol, 16); }
 
 // Pages per split: enough workgroups to fill the chip (about the target count),
 // at least kDecodeMinPages pages each, at most kMaxSplitDecode splits per
@@ -550,28 +577,35 @@ int decode_pages_per_split(const int32_t* T, int B, int64_t ys) {
   return static_cast<int>(pps);
 }
 
-// Launches decode attention for B sequences of lengths T[b] (query at T[b]-1).
-// With k_new/v_new (bf16 path) the same launch writes the token at T[b]-1.
-gqa_status launch_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
-                         const gqa_tensor* o, const int32_t* T, const gqa_tensor* k_new, const gqa_tensor* v_new,
-                         void* workspace, size_t ws_bytes, hipStream_t s) {
+// Splits of a sequence of T keys (one at least, so that a sequence with no
+// query still gets the workgroup that zeroes its padding rows).
+int64_t split_count(int32_t T, int pps) { return std::max<int64_t>(1, ceil_div(ceil_div(T, kPage), pps)); }
+
+// Workspace bytes that suffice for B sequences at ys grid rows, whatever the
+// lengths: pps >= ceil(total_pages * ys / target), so the splits number at
+// most ceil(target / ys) + B.
+size_t ws_bytes_for(const gqa_cache* c, int64_t B, int64_t ys) {
+  const int64_t slots = (ceil_div(kDecodeTargetBlocks, ys) + B) * ys;
+  return static_cast<size_t>(256 + slots * ws_slot_bytes(c->cfg.head_dim));
+}
+
+// Split-T attention over the paged cache for short query runs (one launch per
+// kMaxSeqPerLaunch sequences): the count[b] queries of sequence b, at positions
+// start[b].. in rectangular rows row0[b].., attend to keys 0..position of their
+// own; rows of o outside the run are zeroed.  ncol = (longest run) x (Hq/Hkv).
+// Decode is the run of one query at T-1; with k_new/v_new the launch also
+// writes that token (bf16 only).  Checks (shapes, workspace) are the caller's.
+gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
+                        const gqa_tensor* o, const int32_t* start, const int32_t* count, const int32_t* row0,
+                        int n_rect, int ncol, const gqa_tensor* k_new, const gqa_tensor* v_new, void* workspace,
+                        size_t ws_bytes, hipStream_t s) {
   const gqa_cache_config& cf = c->cfg;
   const int64_t Hq = q->shape[1];
-  const int G = static_cast<int>(Hq / cf.num_kv_heads);
-  const int hchunks = (G + 15) / 16;
-  const int64_t ys = static_cast<int64_t>(cf.num_kv_heads) * hchunks;
-  const int pps = decode_pages_per_split(T, B, ys);
-  int64_t total_splits = 0;
-  for (int b = 0; b < B; ++b) total_splits += ceil_div(ceil_div(T[b], kPage), pps);
-  float* part_o = nullptr;
-  float* part_h = nullptr;
-  int32_t* flags = nullptr;
-  if (total_splits > B) {
-    const WsLayout wl = ws_layout(c, B, Hq);
-    part_o = static_cast<float*>(workspace);
-    part_h = part_o + wl.part_floats;
-    flags = reinterpret_cast<int32_t*>(part_h + wl.hdr_floats);
-  }
+  const int64_t ys = split_ys(c, ncol);
+  std::vector<int32_t> T(B);
+  for (int b = 0; b < B; ++b) T[b] = start[b] + count[b];
+  const int pps = decode_pages_per_split(T.data(), B, ys);
+  const WsView wv = ws_view(workspace, ws_bytes, cf.head_dim);
   gqa_status st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
   int64_t split_base = 0;
@@ -580,9 +614,9 @@ gqa_status launch_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* 
     gqa::DecodeArgs a;
     std::memset(&a, 0, sizeof(a));
     a.q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
-    a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1];
+    a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1]; a.q_s2 = q->stride[2];
     a.o = static_cast<char*>(o->data) + b0 * o->stride[0] * c->elt;
-    a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1];
+    a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1]; a.o_s2 = o->stride[2];
     if (k_new) {
       a.k_new = static_cast<const char*>(k_new->data) + b0 * k_new->stride[0] * c->elt;
       a.kn_s0 = k_new->stride[0]; a.kn_s1 = k_new->stride[1];
@@ -597,28 +631,43 @@ gqa_status launch_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* 
     a.Hkv = cf.num_kv_heads;
     a.d = cf.head_dim;
     a.nseq = nb;
+    a.ncol = ncol;
+    a.n_rect = n_rect;
     a.pages_per_split = pps;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
-    a.part_o = part_o ? part_o + split_base * ys * 16 * cf.head_dim : nullptr;
-    a.part_h = part_h ? part_h + split_base * ys * 16 * 2 : nullptr;
-    a.flags = flags ? flags + split_base * ys * gqa::kDecodeMergers : nullptr;
+    if (wv.slots) {
+      a.part_o = wv.part_o + split_base * ys * 16 * cf.head_dim;
+      a.part_h = wv.part_h + split_base * ys * 16 * 2;
+      a.flags = wv.flags + split_base * ys * gqa::kDecodeMergers;
+    }
     int32_t off = 0;
     for (int j = 0; j < nb; ++j) {
-      a.meta.seq[j] = seq_ids[b0 + j];
-      a.meta.start[j] = T[b0 + j] - 1;
-      a.meta.count[j] = 1;
-      a.meta.row0[j] = 0;
-      a.meta.total[j] = T[b0 + j];
+      const int b = b0 + j;
+      a.meta.seq[j] = seq_ids[b];
+      a.meta.start[j] = start[b];
+      a.meta.count[j] = count[b];
+      a.meta.row0[j] = row0[b];
+      a.meta.total[j] = T[b];
       a.split_off[j] = off;
-      off += static_cast<int>(ceil_div(ceil_div(T[b0 + j], kPage), pps));
+      off += static_cast<int>(split_count(T[b], pps));
     }
     a.split_off[nb] = off;
     hipError_t e = gqa::launch_decode_bf16(a, off, s);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (e != hipSuccess) return hip_fail(e, "split attention launch");
     split_base += off;
   }
   return GQA_OK;
+}
+
+gqa_status launch_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
+                         const gqa_tensor* o, const int32_t* T, const gqa_tensor* k_new, const gqa_tensor* v_new,
+                         void* workspace, size_t ws_bytes, hipStream_t s) {
+  std::vector<int32_t> start(B), count(B, 1), row0(B, 0);
+  for (int b = 0; b < B; ++b) start[b] = T[b] - 1;
+  const int G = static_cast<int>(q->shape[1] / c->cfg.num_kv_heads);
+  return launch_split(c, layer, B, seq_ids, q, o, start.data(), count.data(), row0.data(), 1, G, k_new, v_new,
+                      workspace, ws_bytes, s);
 }
 
 gqa_status launch_decode_f32(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
@@ -670,27 +719,66 @@ gqa_status check_decode_args(const gqa_cache* c, int32_t B, const gqa_tensor* q,
   return check_tensor(o, "o", cf.dtype, B, Hq, 1, cf.head_dim);
 }
 
-gqa_status check_workspace(const gqa_cache* c, int32_t B, int64_t Hq, const int32_t* T, void* workspace,
-                           size_t ws_bytes) {
+// The workspace a split-T call needs: none when every sequence fits one split,
+// else at least `need` bytes (the documented size), 256-byte aligned, with
+// room for the call's split slots.
+gqa_status check_workspace(const gqa_cache* c, int32_t B, int64_t ncol, const int32_t* T, void* workspace,
+                           size_t ws_bytes, size_t need) {
   if (c->cfg.dtype != GQA_BF16 || B == 0) return GQA_OK;
-  const int G = static_cast<int>(Hq / c->cfg.num_kv_heads);
-  const int64_t ys = static_cast<int64_t>(c->cfg.num_kv_heads) * ((G + 15) / 16);
+  const int64_t ys = split_ys(c, ncol);
   const int pps = decode_pages_per_split(T, B, ys);
   int64_t total_splits = 0;
-  for (int b = 0; b < B; ++b) total_splits += ceil_div(ceil_div(T[b], kPage), pps);
+  for (int b = 0; b < B; ++b) total_splits += split_count(T[b], pps);
   if (total_splits <= B) return GQA_OK;
-  const WsLayout wl = ws_layout(c, B, Hq);
-  if (!workspace || ws_bytes < wl.bytes)
-    return fail(GQA_ERR_ARG, "workspace missing or smaller than gqa_workspace_size");
+  if (!workspace || ws_bytes < need) return fail(GQA_ERR_ARG, "workspace missing or smaller than its size query");
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
+  if (ws_view(workspace, ws_bytes, c->cfg.head_dim).slots < total_splits * ys)
+    return fail(GQA_ERR_ARG, "workspace smaller than its size query");
   return GQA_OK;
+}
+
+// Lengths a split-T call reads: start + count keys; a sequence with no query
+// reads none (its single split only zeroes its rows of O).
+std::vector<int32_t> split_lengths(int32_t B, const int32_t* start, const int32_t* count) {
+  std::vector<int32_t> T(B);
+  for (int b = 0; b < B; ++b) T[b] = count[b] ? start[b] + count[b] : 0;
+  return T;
+}
+
+int64_t split_ncol(const gqa_cache* c, int32_t B, int64_t Hq, const int32_t* count) {
+  int32_t longest = 1;
+  for (int b = 0; b < B; ++b) longest = std::max(longest, count[b]);
+  return static_cast<int64_t>(longest) * (Hq / c->cfg.num_kv_heads);
+}
+
+gqa_status check_split_workspace(const gqa_cache* c, int32_t B, int64_t Hq, int64_t n, const int32_t* start,
+                                 const int32_t* count, void* workspace, size_t ws_bytes) {
+  const std::vector<int32_t> T = split_lengths(B, start, count);
+  return check_workspace(c, B, split_ncol(c, B, Hq, count), T.data(), workspace, ws_bytes,
+                         gqa_attention_workspace_size(c, B, static_cast<int32_t>(Hq), static_cast<int32_t>(n)));
+}
+
+gqa_status attend_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* Q,
+                        const gqa_tensor* O, int64_t n, const int32_t* start, const int32_t* count,
+                        const int32_t* row0, void* workspace, size_t ws_bytes, hipStream_t s) {
+  const std::vector<int32_t> T = split_lengths(B, start, count);
+  std::vector<int32_t> st0(B);
+  for (int b = 0; b < B; ++b) st0[b] = T[b] - count[b];
+  return launch_split(c, layer, B, seq_ids, Q, O, st0.data(), count, row0, static_cast<int>(n),
+                      static_cast<int>(split_ncol(c, B, Q->shape[1], count)), nullptr, nullptr, workspace, ws_bytes,
+                      s);
 }
 
 }  // namespace
 
 GQA_EXPORT size_t gqa_workspace_size(const gqa_cache* c, int32_t B, int32_t Hq) {
   if (!c || B < 0 || Hq < 1) return 0;
-  return ws_layout(c, B, Hq).bytes;
+  return ws_bytes_for(c, B, split_ys(c, std::max(1, Hq / c->cfg.num_kv_heads)));
+}
+
+GQA_EXPORT size_t gqa_attention_workspace_size(const gqa_cache* c, int32_t B, int32_t Hq, int32_t n) {
+  if (!c || B < 0 || Hq < 1 || n < 1 || n > GQA_MAX_CHUNK_TOKENS || c->cfg.dtype != GQA_BF16) return 0;
+  return ws_bytes_for(c, B, split_ys(c, static_cast<int64_t>(n) * std::max(1, Hq / c->cfg.num_kv_heads)));
 }
 
 GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
@@ -710,7 +798,8 @@ GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const i
     if (have < 1) return fail(GQA_ERR_CACHE, "decode needs at least one cached token");
   }
   if (B == 0) return GQA_OK;
-  st = check_workspace(c, B, q->shape[1], valid_lengths, workspace, ws_bytes);
+  st = check_workspace(c, B, q->shape[1] / cf.num_kv_heads, valid_lengths, workspace, ws_bytes,
+                       gqa_workspace_size(c, B, static_cast<int32_t>(q->shape[1])));
   if (st != GQA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cf.dtype != GQA_BF16) return launch_decode_f32(c, layer, B, seq_ids, q, o, valid_lengths, s);
@@ -738,7 +827,8 @@ GQA_EXPORT gqa_status gqa_decode_step(gqa_cache* c, int32_t layer, int32_t B, co
   if (plan.n != 1) return fail(GQA_ERR_SHAPE, "k_new and v_new must hold one token: [B, Hkv, 1, d]");
   std::vector<int32_t> T(B);
   for (int b = 0; b < B; ++b) T[b] = pos[b] + 1;
-  st = check_workspace(c, B, q->shape[1], T.data(), workspace, ws_bytes);
+  st = check_workspace(c, B, q->shape[1] / cf.num_kv_heads, T.data(), workspace, ws_bytes,
+                       gqa_workspace_size(c, B, static_cast<int32_t>(q->shape[1])));
   if (st != GQA_OK) return st;
   commit_append(c, layer, B, seq_ids, plan);
   hipStream_t s = static_cast<hipStream_t>(stream);

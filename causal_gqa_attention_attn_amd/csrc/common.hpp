@@ -68,9 +68,9 @@ struct AttnArgs {
 
 struct DecodeArgs {
   const void* q;
-  int64_t q_s0, q_s1;
+  int64_t q_s0, q_s1, q_s2;   // element strides: batch, head, token
   void* o;
-  int64_t o_s0, o_s1;
+  int64_t o_s0, o_s1, o_s2;
   const void* k_new;          // optional new token appended by the same launch: [B][Hkv][1][d]
   int64_t kn_s0, kn_s1;
   const void* v_new;
@@ -80,6 +80,8 @@ struct DecodeArgs {
   const int32_t* table;
   int32_t table_w;
   int32_t Hq, Hkv, d, nseq;
+  int32_t ncol;               // (token, head) columns per kv head: tokens of the longest chunk x Hq/Hkv
+  int32_t n_rect;             // rows of the rectangular q / o (padding rows of o are zeroed)
   int32_t pages_per_split;
   float scale_log2;
   const float* rope;
@@ -87,7 +89,8 @@ struct DecodeArgs {
   float* part_h;              // split (m, l) headers [split][y][16][2]
   int32_t* flags;             // ready flags [split group][merger][split]; zero between calls
   int32_t split_off[kMaxSeqPerLaunch + 1];
-  SeqMeta meta;               // start = T-1, total = T
+  SeqMeta meta;               // start: position of the first query token; count: query tokens;
+                              // row0: their first rectangular row; total: keys read (start + count)
 };
 
 

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   __shared__ int s_ok;
 
   const int G = a.Hq / a.Hkv;
-  const int hchunks = (G + 15) >> 4;
+  const int hchunks = (a.ncol + 15) >> 4;
   const int gy = gridDim.y;
   const int g = blockIdx.y / hchunks;
   const int hcb = blockIdx.y - g * hchunks;
@@ -70,7 +70,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int nsplit = a.split_off[b + 1] - a.split_off[b];
   const int seq = a.meta.seq[b];
   const int T = a.meta.total[b];
-  const int qpos = a.meta.start[b];
+  const int start = a.meta.start[b];
+  const int cnt = a.meta.count[b];
+  const int r0 = a.meta.row0[b];
   const int npages = (T + kPage - 1) / kPage;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(npages, p_begin + a.pages_per_split);
@@ -79,9 +81,39 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
   const int c16 = lane & 15;
-  const int hl = hcb * 16 + c16;           // head within the group held by this lane column
-  const bool hvalid = hl < G;
-  const int Gc = min(16, G - hcb * 16);
+
+  // padding rows of o (rectangular rows outside the sequence's query run) -> 0,
+  // by the first split of the first column chunk of each kv head
+  if (split == 0 && hcb == 0 && a.n_rect > cnt) {
+    for (int idx = threadIdx.x; idx < G * a.n_rect * (D / 8); idx += 256) {
+      const int hh = idx / (a.n_rect * (D / 8));
+      const int rem = idx - hh * a.n_rect * (D / 8);
+      const int rr = rem / (D / 8);
+      const int ch = rem - rr * (D / 8);
+      if (rr < r0 || rr >= r0 + cnt) {
+        uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(g * G + hh) * a.o_s1 +
+                       static_cast<int64_t>(rr) * a.o_s2 + ch * 8;
+        *reinterpret_cast<u32x4*>(op) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  // Columns of the matrix products are (query token t, head h) pairs, column
+  // c = t*G + h; this workgroup holds columns 16*hcb .. 16*hcb + 15.
+  const int Gc = min(16, cnt * G - hcb * 16);   // valid columns of this chunk for this sequence
+  if (Gc <= 0) return;                          // (every split of the chunk returns here)
+  const int cl = hcb * 16 + c16;                // this lane's column
+  const bool hvalid = cl < cnt * G;
+  const int clc = min(cl, cnt * G - 1);
+  const int tl = clc / G;                       // its query token and head
+  const int hl = clc - tl * G;
+  const int qpos = start + tl;                  // the query's position: keys 0..qpos are visible
+  // o row of column c of this chunk
+  auto out_row = [&](int c) {
+    const int col = hcb * 16 + c;
+    const int t = col / G;
+    return static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(g * G + col - t * G) * a.o_s1 +
+           static_cast<int64_t>(r0 + t) * a.o_s2;
+  };
 
   uint16_t* kpool = static_cast<uint16_t*>(a.k_pool);
   uint16_t* vpool = static_cast<uint16_t*>(a.v_pool);
@@ -103,8 +135,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   int64_t phys[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) phys[j] = trow[min(p_first + 4 * j, p_end - 1)];
-  const int hq = g * G + min(hl, G - 1);
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.q_s0 + static_cast<int64_t>(hq) * a.q_s1;
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.q_s0 + static_cast<int64_t>(g * G + hl) * a.q_s1 +
+                         static_cast<int64_t>(r0 + tl) * a.q_s2;
   u32x4 qw[NQ];
 #pragma unroll
   for (int c = 0; c < NQ; ++c) qw[c] = *reinterpret_cast<const u32x4*>(qrow + c * 32 + grp * 8);
@@ -241,10 +273,14 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < NQ; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][c], qf[c], s, 0, 0, 0);
       const int key0 = p * kPage + grp * 4;   // keys of this lane's rows: key0 + i
-      if (p * kPage + kPage > T) {
+      if (p * kPage + kPage > start + 1) {
+        // the page holds keys past the first query's position: causal mask
+        // per column (covers the keys at or past T, since every qpos < T)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (key0 + i >= T) s[i] = -INFINITY;
+          if (key0 + i > qpos) s[i] = -INFINITY;
+      }
+      if (p * kPage + kPage > T) {
         // stale slots past the length: zero their values so 0 * NaN never occurs
         const uint32_t k01 = (key0 < T ? 0x0000ffffu : 0u) | (key0 + 1 < T ? 0xffff0000u : 0u);
         const uint32_t k23 = (key0 + 2 < T ? 0x0000ffffu : 0u) | (key0 + 3 < T ? 0xffff0000u : 0u);
@@ -294,7 +330,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int hh = threadIdx.x >> 4;
   const int dl = threadIdx.x & 15;
   const bool hv2 = hh < Gc;
-  const int h2 = g * G + hcb * 16 + hh;
   float M = red_m[0][hh];
 #pragma unroll
   for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
@@ -318,7 +353,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   if (nsplit == 1) {
     if (!hv2) return;
     const float inv = 1.f / L;
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(h2) * a.o_s1;
+    uint16_t* orow = out_row(hh);
     uint32_t w[E / 2];
 #pragma unroll
     for (int e = 0; e < E / 2; ++e) w[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
@@ -428,7 +463,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   }
   if (pv && f == 0) {
     const float inv = s_ok ? 1.f / Lg : __builtin_nanf("");
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(g * G + hcb * 16 + ph) * a.o_s1;
+    uint16_t* orow = out_row(ph);
     *reinterpret_cast<u32x2*>(orow + 4 * pc) =
         u32x2{pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv)};
   }
@@ -438,8 +473,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int hchunks = (G + 15) / 16;
+  const int hchunks = (a.ncol + 15) / 16;
   dim3 grid(total_splits, a.Hkv * hchunks);
   if (a.d == 128)
     hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(256), 0, s, a);

@@ -57,6 +57,10 @@ typedef enum gqa_status {
 
 typedef enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
 
+/* Longest query run (rectangular rows n) that gqa_prefill / gqa_attention can
+ * send to the split-T kernel: speculative verify chunks and other short runs. */
+#define GQA_MAX_CHUNK_TOKENS 16
+
 /* A strided 4-D device tensor.  stride[] is in elements; stride[3] must be 1.
  * For bf16 the data pointer and stride[0..2] must keep every row 16-byte
  * aligned.  Logical shapes used below:
@@ -146,7 +150,14 @@ gqa_status kv_cache_append(gqa_cache* cache, int32_t layer, int32_t B, const int
  * over the cache slots of the sequence.  With a non-empty cache this is the
  * incremental (suffix) prefill of [P3]: the old prefix is fully visible.
  * Rows of O for padding tokens are written as 0.  Q and O are [B,Hq,n,d] in the
- * cache dtype; accumulation is float32.  workspace may be NULL (ws_bytes 0). */
+ * cache dtype; accumulation is float32.
+ * workspace may be NULL (ws_bytes 0): the query tiles then run on the tiled
+ * kernel.  For a bf16 cache and 1 <= n <= GQA_MAX_CHUNK_TOKENS, a non-NULL
+ * workspace sends the attention to the split-T kernel instead (the decode
+ * kernel with one matrix column per (query token, head), split over the cached
+ * keys, which suits short chunks on long caches); it must then follow the
+ * gqa_decode workspace rule with gqa_attention_workspace_size(cache, B, Hq, n)
+ * bytes.  Both kernels meet the same accuracy; their roundings differ. */
 gqa_status gqa_prefill(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
                        const gqa_tensor* Q, const gqa_tensor* K, const gqa_tensor* V,
                        const uint8_t* valid_mask, const int32_t* positions, const gqa_tensor* O,
@@ -158,7 +169,8 @@ gqa_status gqa_prefill(gqa_cache* cache, int32_t layer, int32_t B, const int32_t
  * `layer`.  The valid tokens of a row must carry consecutive positions
  * p0, p0+1, ... that end at or before the layer's current length; rows of O
  * for padding tokens are written as 0.  gqa_prefill is kv_cache_append
- * followed by this call with p0 = the length before the append. */
+ * followed by this call with p0 = the length before the append.  Same
+ * workspace rule as gqa_prefill. */
 gqa_status gqa_attention(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
                          const gqa_tensor* Q, const uint8_t* valid_mask, const int32_t* positions,
                          const gqa_tensor* O, void* workspace, size_t ws_bytes, void* stream);
@@ -170,9 +182,12 @@ gqa_status gqa_attention(gqa_cache* cache, int32_t layer, int32_t B, const int32
  * q and o are [B,Hq,1,d].  workspace: device scratch for split partials and
  * ready flags, at least gqa_workspace_size(cache, B, Hq) bytes, 256-byte
  * aligned and ZERO-FILLED before its first use (every call leaves its flags at
- * zero again, so one zeroed workspace serves any number of ordered calls).
- * Calls that share a workspace must not overlap in time.  It may be NULL when
- * every sequence fits one split (short caches). */
+ * zero again, so one zeroed workspace serves any number of ordered calls of any
+ * B, Hq or chunk length, provided every call passes the same ws_bytes: its
+ * layout depends only on ws_bytes and d).  Calls that share a workspace must
+ * not overlap in time.  It may be NULL when every sequence fits one split
+ * (short caches).  GQA_ERR_ARG if it is needed and missing, misaligned or too
+ * small. */
 gqa_status gqa_decode(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
                       const gqa_tensor* q, const int32_t* valid_lengths, const gqa_tensor* o,
                       void* workspace, size_t ws_bytes, void* stream);
@@ -214,8 +229,15 @@ gqa_status gqa_cache_check(const gqa_cache* cache);
 
 /* Device workspace bytes that suffice for gqa_decode / gqa_decode_step with up
  * to B sequences and Hq query heads, whatever their lengths (zero-fill it once
- * before first use).  gqa_prefill and gqa_attention need none. */
+ * before first use).  0 for a null cache, B < 0 or Hq < 1. */
 size_t gqa_workspace_size(const gqa_cache* cache, int32_t B, int32_t Hq);
+
+/* Device workspace bytes that suffice for a split-T gqa_prefill / gqa_attention
+ * call with up to B sequences, Hq query heads and n rectangular rows, whatever
+ * the lengths.  0 when that call would not take the split-T kernel (f32 cache,
+ * n < 1 or n > GQA_MAX_CHUNK_TOKENS) or for invalid arguments.  A workspace of
+ * this size also serves gqa_decode for the same B and Hq. */
+size_t gqa_attention_workspace_size(const gqa_cache* cache, int32_t B, int32_t Hq, int32_t n);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* gqa_last_error(void);

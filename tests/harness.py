@@ -47,10 +47,18 @@ class Pair:
         return self.ws
 
     # ------------------------------------------------------------ calls
-    def prefill(self, layer, seq_ids, Q, K, V, mask, pos, oracle=True):
+    def chunk_workspace(self, B, Hq, n):
+        """Workspace for split-T prefill/attention calls (chunks of at most n rows)."""
+        nb = max(self.lib.gqa_attention_workspace_size(self.gpu.handle, B, Hq, n),
+                 self.lib.gqa_workspace_size(self.gpu.handle, B, Hq))
+        if self.ws is None or self.ws.numel() < nb:
+            self.ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        return self.ws
+
+    def prefill(self, layer, seq_ids, Q, K, V, mask, pos, oracle=True, workspace=None):
         dev = [t.to("cuda") for t in (Q, K, V)]
         O = torch.full_like(dev[0], float("nan"))
-        self.lib.gqa_prefill(self.gpu.handle, layer, seq_ids, dev[0], dev[1], dev[2], mask, pos, O)
+        self.lib.gqa_prefill(self.gpu.handle, layer, seq_ids, dev[0], dev[1], dev[2], mask, pos, O, workspace)
         torch.cuda.synchronize()
         ref = None
         if oracle:

@@ -93,6 +93,29 @@ def test_config_checks():
     lib.gqa_cache_destroy(h)
 
 
+def test_workspace_size_queries():
+    """Split-T workspace sizes: zero where no split-T call can happen, enough for
+    the bound on splits otherwise, and the chunk size covers decode's."""
+    import causal_gqa_attention_attn_amd as lib
+    st, h = _cache(lib, num_kv_heads=8, head_dim=128, num_pages=64, max_seqs=4, max_pages_per_seq=16,
+                   max_position=256)
+    assert st == 0
+    assert lib.gqa_attention_workspace_size(h, 4, 32, 0) == 0
+    assert lib.gqa_attention_workspace_size(h, 4, 32, 17) == 0
+    assert lib.gqa_attention_workspace_size(h, -1, 32, 4) == 0
+    assert lib.gqa_workspace_size(h, 4, 0) == 0
+    slot = (16 * 128 + 32 + 4) * 4          # flag row, 16 o rows of d floats, 16 (m, l) headers
+    for B, Hq, n in [(1, 32, 1), (4, 32, 4), (4, 64, 16), (3, 8, 7)]:
+        ys = 8 * -(-(n * (Hq // 8)) // 16)   # kv heads x 16-column chunks
+        want = 256 + (-(-4096 // ys) + B) * ys * slot
+        assert lib.gqa_attention_workspace_size(h, B, Hq, n) == want, (B, Hq, n)
+        assert lib.gqa_attention_workspace_size(h, B, Hq, n) >= lib.gqa_workspace_size(h, B, Hq)
+    lib.gqa_cache_destroy(h)
+    st, h = _cache(lib, dtype=lib.F32)
+    assert lib.gqa_attention_workspace_size(h, 1, 2, 4) == 0, "f32 caches never take the split-T kernel"
+    lib.gqa_cache_destroy(h)
+
+
 def _bad_calls(lib, h):
     """(name, callable) pairs that must fail validation."""
     K = FakeTensor((1, 2, 3, 64))
