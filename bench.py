@@ -26,6 +26,9 @@ truncates between calls), median and minimum of 5 such batches:
   * Llama-shaped prefill: B=8, n=2048, Hq=32, Hkv=8, d=128 (gqa_prefill);
   * serving decode: one gqa_decode_step of 64 sequences with lengths
     log-uniform in [512, 32768] on one layer (about 2.2 GB of K/V);
+  * speculative verify: a 4- and an 8-token chunk appended to and attended
+    over each of those 64 caches (gqa_prefill with a workspace, which takes
+    the split-T kernel), beside the same call on the tiled prefill kernel;
   * edit re-prefill: 16 sequences of 4096 tokens, each truncated at a seeded
     m_b and its suffix re-prefilled (gqa_prefill on a non-empty cache);
     flops 2*Hq*d*(n^2 - m_b^2).
@@ -154,7 +157,7 @@ def other_configs(lib, W):
     lens = W.serving_lengths()
     Bs = len(lens)
     sh = W.SERVING
-    pages = sum(-(-(x + 1) // 16) for x in lens) + 8
+    pages = sum(-(-(x + 16) // 16) for x in lens) + 8
     cache = lib.PagedCache(1, sh.Hkv, sh.d, pages, Bs, 32768 // 16 + 2, dtype=torch.bfloat16, rope_theta=sh.theta,
                            max_position=32770, free_list_order=W.page_order(pages, 1005))
     for b, L in enumerate(lens):
@@ -165,7 +168,9 @@ def other_configs(lib, W):
     st = W.decode_step_inputs(sh, 1005, 0)
     q, k, v = st.q.cuda(), st.k.cuda(), st.v.cuda()
     o = torch.empty_like(q)
-    ws = torch.zeros(lib.gqa_workspace_size(cache.handle, Bs, sh.Hq), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(lib.gqa_workspace_size(cache.handle, Bs, sh.Hq),
+                         lib.gqa_attention_workspace_size(cache.handle, Bs, sh.Hq, 8)), dtype=torch.uint8,
+                     device="cuda")
     ids = list(range(Bs))
     med, mn = _median_ms(lambda: lib.gqa_decode_step(cache.handle, 0, ids, q, k, v, o, ws),
                          before=lambda: [lib.kv_cache_truncate(cache.handle, b, lens[b]) for b in ids])
@@ -175,6 +180,27 @@ def other_configs(lib, W):
                                          "Hq=32 Hkv=8 d=128, one layer",
                              "kv_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                              "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1)}
+    # speculative verify: a chunk of n draft tokens per sequence on the same caches,
+    # split-T kernel (with workspace) beside the tiled prefill kernel (without)
+    for n in (4, 8):
+        chunk = W.prefill_inputs(W.AttnShape(B=Bs, n=n, Hq=sh.Hq, Hkv=sh.Hkv, d=sh.d, dtype=sh.dtype,
+                                             theta=sh.theta), 1007 + n, start=lens)
+        Qc, Kc, Vc = chunk.Q.cuda(), chunk.K.cuda(), chunk.V.cuda()
+        Oc = torch.empty_like(Qc)
+        trunc = lambda: [lib.kv_cache_truncate(cache.handle, b, lens[b]) for b in ids]
+        med, mn = _median_ms(lambda: lib.gqa_prefill(cache.handle, 0, ids, Qc, Kc, Vc, chunk.mask, chunk.positions,
+                                                     Oc, ws), before=trunc)
+        tmed, _ = _median_ms(lambda: lib.gqa_prefill(cache.handle, 0, ids, Qc, Kc, Vc, chunk.mask, chunk.positions,
+                                                      Oc), before=trunc, iters=5, reps=3)
+        nbytes = sum((L + n) * 2 * sh.Hkv * sh.d * 2 for L in lens)
+        gbs = nbytes / (med * 1e-3) / 1e9
+        res[f"verify_chunk_n{n}"] = {
+            "workload": f"gqa_prefill of a {n}-token chunk on each of the 64 serving caches (append + attention), "
+                        "Hq=32 Hkv=8 d=128, one layer, split-T kernel",
+            "kv_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1),
+            "tiled_kernel_us_median": round(tmed * 1e3, 1)}
+    trunc = None
     cache.close()
     # edit re-prefill
     sh = W.EDIT

@@ -1,10 +1,17 @@
-// bfloat16 split-T decode attention over the paged cache, one launch per layer.
+// bfloat16 split-T attention over the paged cache for decode and short query
+// chunks, one launch per layer.
 //
 // What it computes (page "模型执行：从 token 到 Prefill 与 Decode", prefill and
 // decode shapes; page "KV Cache 与 Prefill/Decode 推理路径", single-token
 // decode needs no mask): one new query per sequence, at position T-1, attends
 // to all T cached slots of its KV head g(h) = floor(h*Hkv/Hq):
 //   o[b,h] = sum_{j<T} softmax_j(<rot(q), k_used[g,j]>/sqrt(d)) v[g,j].
+// More generally a sequence brings a run of `count` queries at positions
+// start, start+1, ... (a verify chunk, or rows inside a cached sequence; page
+// "Prefill：整层状态演化与 KV 建立", 2.3 causal mask): the query at position p
+// attends to slots 0..p only.  Each (query token t, head h) pair is one matrix
+// column c = t*G + h, with its own rotation row and causal limit; decode is the
+// run of one.  Rectangular rows of o outside the run are written as 0.
 // Optionally the same launch first appends the step's new token (slot T-1):
 // its key is rotated with the query's rotation row (same position) and
 // rounded to bf16, its value copied, both written to the cache and used
@@ -12,14 +19,14 @@
 //
 // How (memory-bound; every K/V byte is read from HBM once per step):
 //  * one workgroup = (sequence, split of consecutive pages, kv head, up to 16
-//    query heads of its group); its four waves take the split's pages in turn,
+//    (token, head) columns of its group); its four waves take the split's pages in turn,
 //    each with two pages in flight; the block-table entries, the query
 //    and its rotation row are requested together before any is used;
-//  * per page: S^T[16 keys x 16 heads] = K q^T on v_mfma_f32_16x16x32_bf16 with
+//  * per page: S^T[16 keys x 16 columns] = K q^T on v_mfma_f32_16x16x32_bf16 with
 //    the K rows loaded straight from the page, then O^T[d x heads] += V^T P^T
 //    on v_mfma_f32_16x16x16_bf16 with V^T read straight from the d-major page;
 //    the score accumulator is already the B operand of the second product;
-//  * online softmax in base 2 per head; the four waves, then the splits, are
+//  * online softmax in base 2 per column; the four waves, then the splits, are
 //    combined with the log-sum-exp rule: with M = max_s m_s,
 //    O = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);
 //  * split combine inside the launch, without atomics (same-address
