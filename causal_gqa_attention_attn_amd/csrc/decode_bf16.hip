@@ -33,7 +33,7 @@
 //    device-scope atomics serialise across the chip's XCDs): every split
 //    writes its (m, l, o) record with device-scope stores and then a ready flag
 //    for each merger.  The mergers are the last (up to four) splits of the
-//    (sequence, kv head) - the highest workgroup indices of the group, so they
+//    (sequence, kv head, column chunk) - the highest workgroup indices of the group, so they
 //    only wait on workgroups dispatched before them or on each other, and
 //    there are never more of them than the chip holds at once.  Each polls its
 //    flags with a bounded spin, combines its share of the output columns and
@@ -68,12 +68,21 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 
   const int G = a.Hq / a.Hkv;
   const int hchunks = (a.ncol + 15) >> 4;
-  const int gy = gridDim.y;
-  const int g = blockIdx.y / hchunks;
-  const int hcb = blockIdx.y - g * hchunks;
+  const int gy = a.Hkv * hchunks;          // (kv head, column chunk) rows of the split records
+  // blockIdx.x = (block of 8 consecutive splits, column chunk, split in the
+  // block): the column chunks of one split are 8 workgroups apart, so they
+  // run on the same XCD (workgroup index mod 8) one shortly after another and
+  // the later ones find the split's pages in that XCD's L2.
+  const int xb = blockIdx.x / (8 * hchunks);
+  const int xr = blockIdx.x - xb * 8 * hchunks;
+  const int hcb = xr >> 3;
+  const int gsplit = xb * 8 + (xr & 7);
+  if (gsplit >= a.split_off[a.nseq]) return;   // padding of the last block of 8
+  const int g = blockIdx.y;
+  const int yrow = g * hchunks + hcb;
   int b = 0;
-  while (b + 1 < a.nseq && a.split_off[b + 1] <= static_cast<int>(blockIdx.x)) ++b;
-  const int split = blockIdx.x - a.split_off[b];
+  while (b + 1 < a.nseq && a.split_off[b + 1] <= gsplit) ++b;
+  const int split = gsplit - a.split_off[b];
   const int nsplit = a.split_off[b + 1] - a.split_off[b];
   const int seq = a.meta.seq[b];
   const int T = a.meta.total[b];
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     return;
   }
 
-  // Split records of this (sequence, blockIdx.y): o rows [split][head in chunk][D]
+  // Split records of this (sequence, kv head, column chunk): o rows [split][column in chunk][D]
   // and (m, l) headers [split][head in chunk], written and read with
   // device-scope (sc1) buffer accesses, which stay coherent across the XCDs'
   // L2 caches.  The last K splits are also mergers: merger j combines output
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   // merger, so a merger clears its own row without racing another's wait.
   const int K = nsplit >= kDecodeMergers ? kDecodeMergers : 2;   // divides D/4
   const int mj = split - (nsplit - K);          // merger index, negative for the others
-  const int64_t group = static_cast<int64_t>(a.split_off[b]) * gy + static_cast<int64_t>(blockIdx.y) * nsplit;
+  const int64_t group = static_cast<int64_t>(a.split_off[b]) * gy + static_cast<int64_t>(yrow) * nsplit;
   int32_t* flags = a.flags + group * kDecodeMergers;
   const __amdgpu_buffer_rsrc_t ro =
       __builtin_amdgcn_make_buffer_rsrc(a.part_o + group * (16 * D), 0, nsplit * Gc * D * 4, kBufferWord3);
@@ -481,7 +490,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s) {
   const int hchunks = (a.ncol + 15) / 16;
-  dim3 grid(total_splits, a.Hkv * hchunks);
+  dim3 grid(((total_splits + 7) / 8) * 8 * hchunks, a.Hkv);
   if (a.d == 128)
     hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(256), 0, s, a);
   else
