@@ -22,7 +22,12 @@ Test infrastructure.  Sources:
   - prompt-edit lesson: after an edit at position m keep every layer's KV for
     [0, m), drop the rest, and run an incremental prefill on the suffix;
   - decode lessons: a single new token appends one K/V per layer and reads all
-    T cached entries, with no future entry to mask.
+    T cached entries, with no future entry to mask;
+  - prefix-sharing lesson: requests whose first m token ids agree have equal
+    per-layer K/V on positions 0..m-1 and may reference the same cache blocks;
+    the system counts the references, and a shared block returns to the free
+    pool only once no request references it; a fork inside a block is a
+    matter of page granularity and copy-on-write.
 * page "模型执行：从 token 到 Prefill 与 Decode": the decode step appends, then
   attends over T = (cached) + 1 entries.
 
@@ -35,7 +40,15 @@ Readings fixed here (the pages leave them open):
   logical page takes it; pages are taken from the front of the free list in
   batch order, then logical-page order; pages freed by truncation go to the
   back in ascending logical order, remapped source pages in the order given;
-* invalid (padding) query rows produce exact zeros.
+* invalid (padding) query rows produce exact zeros;
+* a fork (sequence dst takes sequence src's positions [0, m)) makes dst's
+  first ceil(m/P) table entries the same physical pages as src's, each page
+  counting one more reference; nothing is copied then.  A write into a page
+  with more than one reference (only possible into the page that holds slot
+  c_b when c_b is not a multiple of P) first copies that page, every layer,
+  to a page taken from the front of the free list and points the writer's
+  entry at the copy: in batch order, a row's copy is taken before its new
+  pages.  A page reaches the free list when its last reference goes.
 """
 from collections import deque
 
@@ -91,6 +104,8 @@ class CacheModel:
         if sorted(order) != list(range(num_pages)):
             raise OracleError("ARG", "free-list order must be a permutation of the pool")
         self.free = deque(order)
+        self.ref = [0] * num_pages          # table entries that reference each page
+        self.copies = []                    # (src, dst) page copies made by copy-on-write, in order
         self.pages = {s: [] for s in range(max_seqs)}
         self.length = {(s, l): 0 for s in range(max_seqs) for l in range(num_layers)}
         empty = np.zeros((num_kv_heads, 0, head_dim), dtype=np.float32)
@@ -117,16 +132,24 @@ class CacheModel:
     def check(self) -> list:
         """Violations of the cache invariants (empty when consistent)."""
         bad = []
-        owned = []
+        refs = [0] * self.num_pages
         for s in range(self.max_seqs):
             lens = [self.length[(s, l)] for l in range(self.L)]
             if len(set(lens)) > 1:
                 bad.append(f"sequence {s}: layer lengths differ {lens}")
             if len(self.pages[s]) != _ceil_div(max(lens), self.P):
                 bad.append(f"sequence {s}: {len(self.pages[s])} pages for length {max(lens)}")
-            owned += self.pages[s]
-        if sorted(owned + list(self.free)) != list(range(self.num_pages)):
-            bad.append("pages are lost or owned twice")
+            if len(set(self.pages[s])) != len(self.pages[s]):
+                bad.append(f"sequence {s}: a page appears twice in its table")
+            for p in self.pages[s]:
+                refs[p] += 1
+        if refs != self.ref:
+            bad.append("reference counts differ from the tables")
+        free = list(self.free)
+        if len(set(free)) != len(free) or any(refs[p] for p in free):
+            bad.append("a free page is listed twice or still referenced")
+        if sorted(free + [p for p in range(self.num_pages) if refs[p]]) != list(range(self.num_pages)):
+            bad.append("pages are lost")
         return bad
 
     # ------------------------------------------------------------ checks
@@ -169,17 +192,38 @@ class CacheModel:
             if _ceil_div(c + nb, self.P) > self.max_pages_per_seq:
                 raise OracleError("OUT_OF_PAGES", "sequence exceeds its block-table capacity")
         need = []
+        ref = list(self.ref)        # references as the rows before this one leave them
         for b, (s, nb) in enumerate(runs):
             c = self.length[(ids[b], layer)]
-            need.append(max(0, _ceil_div(c + nb, self.P) - len(self.pages[ids[b]])))
-        if sum(need) > len(self.free):
+            # writing from slot c touches an existing page only when c is inside
+            # one; that page is copied first if another table references it
+            cow = nb > 0 and c % self.P != 0 and self._copy_on_write(ref, self.pages[ids[b]][c // self.P])
+            if cow:
+                ref[self.pages[ids[b]][c // self.P]] -= 1
+            need.append((cow, max(0, _ceil_div(c + nb, self.P) - len(self.pages[ids[b]]))))
+        if sum(int(cow) + k for cow, k in need) > len(self.free):
             raise OracleError("OUT_OF_PAGES", "not enough free pages")
         return runs, need
 
+    @staticmethod
+    def _copy_on_write(ref, page) -> bool:
+        """A page must be copied before a write when another table references it."""
+        return ref[page] > 1
+
     def _commit_append(self, layer, ids, K, V, runs, need):
-        for b, k in enumerate(need):
+        for b, (cow, k) in enumerate(need):
+            table = self.pages[ids[b]]
+            if cow:
+                lp = self.length[(ids[b], layer)] // self.P
+                new = self.free.popleft()
+                self.copies.append((table[lp], new))
+                self.ref[table[lp]] -= 1
+                self.ref[new] = 1
+                table[lp] = new
             for _ in range(k):
-                self.pages[ids[b]].append(self.free.popleft())
+                page = self.free.popleft()
+                self.ref[page] = 1
+                table.append(page)
         for b, (s, nb) in enumerate(runs):
             if nb == 0:
                 continue
@@ -276,9 +320,32 @@ class CacheModel:
             self.K[key] = self.K[key][:, :n]
             self.V[key] = self.V[key][:, :n]
         keep = _ceil_div(max(self.length[(seq, l)] for l in range(self.L)), self.P)
-        freed = self.pages[seq][keep:]
+        dropped = self.pages[seq][keep:]
         self.pages[seq] = self.pages[seq][:keep]
-        self.free.extend(freed)
+        for p in dropped:
+            self.ref[p] -= 1
+            if self.ref[p] == 0:
+                self.free.append(p)
+
+    def fork(self, src, dst, m):
+        """Sequence dst (empty) takes src's positions [0, m) in every layer by
+        referencing src's first ceil(m/P) pages; no page is copied."""
+        if not (0 <= src < self.max_seqs and 0 <= dst < self.max_seqs) or src == dst:
+            raise OracleError("ARG", "bad sequence ids")
+        if m < 0:
+            raise OracleError("ARG", "negative fork length")
+        if self.pages[dst] or any(self.length[(dst, l)] for l in range(self.L)):
+            raise OracleError("CACHE", "the destination sequence is not empty")
+        if m > min(self.length[(src, l)] for l in range(self.L)):
+            raise OracleError("POSITION", "fork length beyond the source's length")
+        self.pages[dst] = list(self.pages[src][:_ceil_div(m, self.P)])
+        for p in self.pages[dst]:
+            self.ref[p] += 1
+        for l in range(self.L):
+            key_s, key_d = (src, l), (dst, l)
+            self.K[key_d] = self.K[key_s][:, :m].copy()
+            self.V[key_d] = self.V[key_s][:, :m].copy()
+            self.length[key_d] = m
 
     def remap(self, src, dst):
         """Move owned pages src[i] to free pages dst[i]; logical content is unchanged."""
@@ -288,20 +355,21 @@ class CacheModel:
             raise OracleError("ARG", "src and dst differ in length")
         if len(set(src)) != len(src) or len(set(dst)) != len(dst):
             raise OracleError("ARG", "repeated page")
-        owner = {}
-        for s, pl in self.pages.items():
-            for i, p in enumerate(pl):
-                owner[p] = (s, i)
         free = set(self.free)
         for a, b in zip(src, dst):
             if not (0 <= a < self.num_pages and 0 <= b < self.num_pages):
                 raise OracleError("ARG", "page id out of range")
-            if a not in owner:
+            if self.ref[a] == 0:
                 raise OracleError("CACHE", "source page is not in use")
             if b not in free:
                 raise OracleError("CACHE", "destination page is not free")
+        moved = dict(zip(src, dst))
+        for pl in self.pages.values():
+            for i, p in enumerate(pl):
+                if p in moved:
+                    pl[i] = moved[p]
         for a, b in zip(src, dst):
-            s, i = owner[a]
-            self.pages[s][i] = b
+            self.ref[b] = self.ref[a]
+            self.ref[a] = 0
             self.free.remove(b)
         self.free.extend(src)

@@ -9,12 +9,14 @@ import numpy as np
 import pytest
 
 from oracle import attention, bf16, rope
+from oracle.cache_model import CacheModel, _ceil_div
 import test_oracle_pins as pins
 
 ALL_PINS = [pins.check_worked_example, pins.check_single_key_and_uniform,
             pins.check_against_textbook_sdpa, pins.check_brute_force,
             pins.check_mask_counts, pins.check_bf16_rounding, pins.check_rotation,
-            pins.check_cache_counts]
+            pins.check_cache_counts, pins.check_prefix_sharing,
+            pins.check_fork_then_suffix_equals_full_prefill]
 
 
 def _some_pin_fails():
@@ -93,6 +95,33 @@ def _bf16_truncate(x):
     return (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).copy()
 
 
+def _truncate_ignoring_references(self, seq, m):
+    """Frees every dropped page, even one another sequence still references."""
+    for l in range(self.L):
+        key = (seq, l)
+        n = min(self.length[key], m)
+        self.length[key] = n
+        self.K[key] = self.K[key][:, :n]
+        self.V[key] = self.V[key][:, :n]
+    keep = _ceil_div(max(self.length[(seq, l)] for l in range(self.L)), self.P)
+    dropped = self.pages[seq][keep:]
+    self.pages[seq] = self.pages[seq][:keep]
+    for p in dropped:
+        self.ref[p] = 0
+        self.free.append(p)
+
+
+_fork = CacheModel.fork
+
+
+def _fork_whole_pages_only(self, src, dst, m):
+    """References floor(m/P) pages: the partly filled block of a mid-block fork is lost."""
+    _fork(self, src, dst, m)
+    for p in self.pages[dst][m // self.P:]:
+        self.ref[p] -= 1
+    self.pages[dst] = self.pages[dst][:m // self.P]
+
+
 MUTANTS = {
     "head_map_modulo": (attention, "head_map", lambda h, Hq, Hkv: h % Hkv),
     "mask_strict": (attention, "slot_mask",
@@ -107,6 +136,9 @@ MUTANTS = {
     "rotation_sign": (rope, "rotate", _rotate_sign),
     "rotation_adjacent_pairs": (rope, "rotate", _rotate_adjacent),
     "bf16_truncation": (bf16, "round_f32_to_bf16", _bf16_truncate),
+    "no_copy_on_write": (CacheModel, "_copy_on_write", staticmethod(lambda ref, page: False)),
+    "shared_page_freed_on_truncate": (CacheModel, "truncate", _truncate_ignoring_references),
+    "fork_whole_pages_only": (CacheModel, "fork", _fork_whole_pages_only),
 }
 
 

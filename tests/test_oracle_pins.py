@@ -303,6 +303,83 @@ def test_allocator_order_and_truncate():
     assert m.check() == []
 
 
+def check_prefix_sharing():
+    """Prefix-sharing lesson of "KV Cache 与 Prefill/Decode 推理路径": requests with
+    the same first m tokens have the same per-layer K/V there, so the second
+    one references the first one's blocks instead of prefilling them again; a
+    shared block goes back to the pool only when no request references it; a
+    fork inside a block (its 18-token, two-block example) needs the block
+    copied before either branch writes into it."""
+    rng = np.random.default_rng(11)
+    m = _model(num_layers=2, num_pages=10, max_seqs=3)
+    for layer in range(2):
+        _append(m, layer, [0], [18], [0], rng)
+    assert m.page_table(0) == [0, 1]
+    m.fork(0, 1, 18)
+    assert m.page_table(1) == [0, 1], "the fork references the prefix blocks"
+    assert len(m.free) == 8 and m.ref[:2] == [2, 2] and m.copies == []
+    for layer in range(2):
+        assert np.array_equal(m.keys(1, layer), m.keys(0, layer))
+        assert np.array_equal(m.values(1, layer), m.values(0, layer))
+    # branch 1 writes slot 18, inside shared block 1: copied first, to the next free page
+    suffix = []
+    for layer in range(2):
+        suffix.append(_append(m, layer, [1], [3], [18], rng))
+    assert m.page_table(1) == [0, 2] and m.copies == [(1, 2)]
+    assert m.ref[:3] == [2, 1, 1]
+    # branch 0 writes slot 18 too: block 1 has one reference left, written in place
+    for layer in range(2):
+        _append(m, layer, [0], [5], [18], rng)
+    assert m.page_table(0) == [0, 1] and m.copies == [(1, 2)]
+    for layer in range(2):
+        assert np.array_equal(m.keys(1, layer)[:, :18], m.keys(0, layer)[:, :18])
+        assert np.array_equal(m.keys(1, layer)[:, 18:], suffix[layer][0][0])
+        assert np.array_equal(m.values(1, layer)[:, 18:], suffix[layer][1][0])
+    assert m.check() == []
+    # releasing branch 0 frees only its own block; the shared block 0 stays
+    m.truncate(0, 0)
+    assert list(m.free)[-1] == 1 and 0 not in m.free and m.ref[0] == 1
+    m.truncate(1, 0)
+    assert list(m.free)[-2:] == [0, 2] and m.check() == []
+    # a fork at a block boundary shares whole blocks only and needs no copy
+    for layer in range(2):
+        _append(m, layer, [2], [32], [0], rng)
+    m.fork(2, 0, 16)
+    for layer in range(2):
+        _append(m, layer, [0], [4], [16], rng)
+    assert len(m.page_table(0)) == 2 and m.page_table(0)[0] == m.page_table(2)[0]
+    assert m.copies == [(1, 2)] and m.check() == []
+
+
+def check_fork_then_suffix_equals_full_prefill():
+    """A forked request that prefills only its own suffix gets the outputs a full
+    prefill of the whole sequence gets (position i depends on tokens 0..i only)."""
+    rng = np.random.default_rng(12)
+    Hq, Hkv, d, n, mfork = 4, 2, 8, 40, 21
+    Q = rng.standard_normal((1, Hq, n, d)).astype(np.float32)
+    K = rng.standard_normal((1, Hkv, n, d)).astype(np.float32)
+    V = rng.standard_normal((1, Hkv, n, d)).astype(np.float32)
+    pos = np.arange(n)[None].astype(np.int32)
+    full = _model(num_kv_heads=Hkv, head_dim=d, rope_theta=1e4, max_seqs=3)
+    O_full = full.prefill(0, [0], Q, K, V, np.ones((1, n), np.uint8), pos)
+    m = _model(num_kv_heads=Hkv, head_dim=d, rope_theta=1e4, max_seqs=3)
+    other = rng.standard_normal((1, Hkv, n, d)).astype(np.float32)
+    head = np.ones((1, n), np.uint8)
+    head[:, mfork:] = 0
+    m.prefill(0, [0], Q, K, V, head, pos)                    # the shared prefix, as request 0
+    tail = np.concatenate([K[:, :, :mfork], other[:, :, mfork:]], axis=2)
+    m.append(0, [0], tail, tail, 1 - head, pos)              # request 0 continues differently
+    m.fork(0, 1, mfork)
+    O_sfx = m.prefill(0, [1], Q, K, V, 1 - head, pos)
+    assert np.allclose(O_sfx[:, :, mfork:], O_full[:, :, mfork:], rtol=0, atol=1e-12)
+    assert m.check() == []
+
+
+def test_prefix_sharing():
+    check_prefix_sharing()
+    check_fork_then_suffix_equals_full_prefill()
+
+
 def test_remap_keeps_logical_content():
     rng = np.random.default_rng(0)
     m = _model(num_pages=8)
