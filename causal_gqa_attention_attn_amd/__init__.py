@@ -32,7 +32,7 @@ F32, BF16 = 0, 1
 STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "MASK", -5: "POSITION",
           -6: "CACHE", -7: "OUT_OF_PAGES", -8: "UNSUPPORTED", -9: "HIP"}
 EXPORTS = ["gqa_cache_buffer_sizes", "gqa_cache_create", "gqa_cache_destroy", "kv_cache_append",
-           "gqa_prefill", "gqa_attention", "gqa_decode", "gqa_decode_step", "kv_cache_truncate", "kv_cache_remap", "gqa_cache_length",
+           "gqa_prefill", "gqa_attention", "gqa_decode", "gqa_decode_step", "kv_cache_truncate", "kv_cache_fork", "kv_cache_remap", "gqa_cache_length",
            "gqa_cache_page_table", "gqa_cache_free_pages", "gqa_cache_check", "gqa_workspace_size",
            "gqa_attention_workspace_size",
            "gqa_last_error"]
@@ -75,6 +75,7 @@ _sig = {
     "gqa_decode": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _P, _TP, _P, ctypes.c_size_t, _P],
     "gqa_decode_step": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _TP, _TP, _TP, _P, ctypes.c_size_t, _P],
     "kv_cache_truncate": [_P, ctypes.c_int32, ctypes.c_int32],
+    "kv_cache_fork": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
     "kv_cache_remap": [_P, ctypes.c_int32, _P, _P, _P],
     "gqa_cache_length": [_P, ctypes.c_int32, ctypes.c_int32, _I32P],
     "gqa_cache_page_table": [_P, ctypes.c_int32, _P, ctypes.c_int32, _I32P],
@@ -220,6 +221,10 @@ def gqa_decode_step(handle, layer, seq_ids, q, k_new, v_new, o, workspace=None, 
 
 def kv_cache_truncate(handle, seq_id, m):
     _check(_lib.kv_cache_truncate(handle, seq_id, m), "kv_cache_truncate")
+
+
+def kv_cache_fork(handle, src_seq, dst_seq, m):
+    _check(_lib.kv_cache_fork(handle, src_seq, dst_seq, m), "kv_cache_fork")
 
 
 def kv_cache_remap(handle, src_pages, dst_pages, stream=None):

@@ -17,6 +17,14 @@
 //    logical page takes it from the front of the free list, in batch order then
 //    logical-page order; truncation returns pages to the back in ascending
 //    logical order, remap returns source pages in the order given;
+//  * a page may be referenced by several sequences' tables (kv_cache_fork); it
+//    counts its references and returns to the back of the free list when the
+//    last one goes.  A write into a page with more than one reference first
+//    copies the page (every layer) to a page from the front of the free list
+//    and points the writer's entry at the copy, in batch order, a row's copy
+//    before its new pages ([P3] prefix-sharing lesson: shared blocks live until
+//    no request references them; a fork inside a block is a question of
+//    copy-on-write);
 //  * every check runs before any state changes or any launch.
 #include <algorithm>
 #include <cmath>
@@ -46,6 +54,8 @@ struct gqa_cache {
   std::vector<float> rope_host;             // [max_position][d/2][2]
   bool rope_uploaded = false;
   std::vector<std::pair<int32_t, int32_t>> pending;  // block-table entries to write on the device
+  std::vector<std::pair<int32_t, int32_t>> copies;   // (src, dst) page copies to make before the next write
+  std::vector<int32_t> ref;                 // table entries that reference each page (0 = free)
   int elt = 2;
   int64_t layer_elems = 0;                  // elements of one layer of a pool
   int64_t page_elems = 0;                   // elements of one page (all kv heads) of one layer
@@ -151,6 +161,7 @@ gqa_status valid_run(const uint8_t* m, int64_t n, int64_t* row0, int64_t* count)
 struct AppendPlan {
   int64_t n = 0;
   std::vector<int32_t> row0, count, start, need;
+  std::vector<uint8_t> cow;                 // the row's first write lands in a shared page: copy it first
 };
 
 // Every check of an append (mask, positions, capacity, page budget).
@@ -170,6 +181,7 @@ gqa_status plan_append(const gqa_cache* c, int32_t layer, int32_t B, const int32
   plan->count.assign(B, 0);
   plan->start.assign(B, 0);
   plan->need.assign(B, 0);
+  plan->cow.assign(B, 0);
   for (int b = 0; b < B; ++b) {
     int64_t run0 = 0, cnt = 0;
     gqa_status sr = valid_run(mask + static_cast<int64_t>(b) * n, n, &run0, &cnt);
@@ -190,9 +202,20 @@ gqa_status plan_append(const gqa_cache* c, int32_t layer, int32_t B, const int32
       return fail(GQA_ERR_OUT_OF_PAGES, "sequence exceeds its block-table capacity");
   }
   int64_t total_need = 0;
+  std::vector<int32_t> released;            // shared pages that earlier rows of this call copy away from
   for (int b = 0; b < B; ++b) {
     const int s = seq_ids[b];
-    const int64_t end = static_cast<int64_t>(plan->start[b]) + plan->count[b];
+    const int32_t c0 = plan->start[b];
+    if (plan->count[b] > 0 && c0 % kPage != 0) {
+      const int32_t page = c->pages[s][c0 / kPage];
+      const int32_t refs = c->ref[page] - static_cast<int32_t>(std::count(released.begin(), released.end(), page));
+      if (refs > 1) {
+        plan->cow[b] = 1;
+        released.push_back(page);
+        ++total_need;
+      }
+    }
+    const int64_t end = static_cast<int64_t>(c0) + plan->count[b];
     const int64_t have = static_cast<int64_t>(c->pages[s].size());
     plan->need[b] = static_cast<int32_t>(std::max<int64_t>(0, ceil_div(end, kPage) - have));
     total_need += plan->need[b];
@@ -205,11 +228,23 @@ void commit_append(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_id
   const gqa_cache_config& cf = c->cfg;
   for (int b = 0; b < B; ++b) {
     const int s = seq_ids[b];
+    if (plan.cow[b]) {
+      const int32_t lp = plan.start[b] / kPage;
+      const int32_t old = c->pages[s][lp];
+      const int32_t page = c->free_list.front();
+      c->free_list.pop_front();
+      c->copies.emplace_back(old, page);
+      --c->ref[old];
+      c->ref[page] = 1;
+      c->pages[s][lp] = page;
+      c->pending.emplace_back(s * cf.max_pages_per_seq + lp, page);
+    }
     for (int k = 0; k < plan.need[b]; ++k) {
       const int32_t page = c->free_list.front();
       c->free_list.pop_front();
       const int32_t lp = static_cast<int32_t>(c->pages[s].size());
       c->pages[s].push_back(page);
+      c->ref[page] = 1;
       c->pending.emplace_back(s * cf.max_pages_per_seq + lp, page);
     }
   }
@@ -221,13 +256,54 @@ gqa_status hip_fail(hipError_t e, const char* what) {
   return fail(GQA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Upload the rotation table once and write pending block-table entries.
+gqa_status launch_copies(gqa_cache* c, const std::vector<std::pair<int32_t, int32_t>>& copies, hipStream_t s) {
+  for (size_t i0 = 0; i0 < copies.size(); i0 += gqa::kMaxPatchPerLaunch) {
+    gqa::CopyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k_pool = c->k_pool;
+    a.v_pool = c->v_pool;
+    a.layer_stride = c->layer_elems;
+    a.page_elems = c->page_elems;
+    a.elt_bytes = c->elt;
+    a.n = static_cast<int32_t>(std::min<size_t>(copies.size() - i0, gqa::kMaxPatchPerLaunch));
+    for (int j = 0; j < a.n; ++j) {
+      a.src[j] = copies[i0 + j].first;
+      a.dst[j] = copies[i0 + j].second;
+    }
+    hipError_t e = gqa::launch_page_copy(a, c->cfg.num_layers, s);
+    if (e != hipSuccess) return hip_fail(e, "page copy launch");
+  }
+  return GQA_OK;
+}
+
+// Upload the rotation table once, make pending copy-on-write page copies and
+// write pending block-table entries.
 gqa_status sync_metadata(gqa_cache* c, hipStream_t s) {
   if (c->cfg.rope_style == 1 && !c->rope_uploaded) {
     hipError_t e = hipMemcpyAsync(c->d_rope, c->rope_host.data(), c->rope_host.size() * sizeof(float),
                                   hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "rotation table upload");
     c->rope_uploaded = true;
+  }
+  if (!c->copies.empty()) {
+    gqa_status st = launch_copies(c, c->copies, s);
+    if (st != GQA_OK) return st;
+    c->copies.clear();
+  }
+  // one write per table entry, the last one queued (a fork's entry may be
+  // replaced by its copy in the same call, and a patch launch writes its
+  // entries in parallel)
+  if (c->pending.size() > 1) {
+    std::vector<std::pair<int32_t, int32_t>> last;
+    last.reserve(c->pending.size());
+    std::vector<std::pair<int32_t, int32_t>> sorted(c->pending);
+    std::stable_sort(sorted.begin(), sorted.end(),
+                     [](const std::pair<int32_t, int32_t>& x, const std::pair<int32_t, int32_t>& y) {
+                       return x.first < y.first;
+                     });
+    for (size_t k = 0; k < sorted.size(); ++k)
+      if (k + 1 == sorted.size() || sorted[k + 1].first != sorted[k].first) last.push_back(sorted[k]);
+    c->pending.swap(last);
   }
   size_t i = 0;
   while (i < c->pending.size()) {
@@ -393,6 +469,7 @@ GQA_EXPORT gqa_status gqa_cache_create(const gqa_cache_config* cfg, void* k_pool
   c->d_table = page_table;
   c->d_rope = static_cast<float*>(rope_table);
   c->free_list.assign(order.begin(), order.end());
+  c->ref.assign(cfg->num_pages, 0);
   c->pages.assign(cfg->max_seqs, {});
   c->len.assign(static_cast<size_t>(cfg->max_seqs) * cfg->num_layers, 0);
   c->elt = cfg->dtype == GQA_BF16 ? 2 : 4;
@@ -857,8 +934,33 @@ GQA_EXPORT gqa_status kv_cache_truncate(gqa_cache* c, int32_t seq_id, int32_t m)
   }
   const size_t keep = static_cast<size_t>(ceil_div(longest, kPage));
   std::vector<int32_t>& pl = c->pages[seq_id];
-  for (size_t i = keep; i < pl.size(); ++i) c->free_list.push_back(pl[i]);
+  for (size_t i = keep; i < pl.size(); ++i)
+    if (--c->ref[pl[i]] == 0) c->free_list.push_back(pl[i]);
   if (pl.size() > keep) pl.resize(keep);
+  return GQA_OK;
+}
+
+GQA_EXPORT gqa_status kv_cache_fork(gqa_cache* c, int32_t src, int32_t dst, int32_t m) {
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const gqa_cache_config& cf = c->cfg;
+  if (src < 0 || src >= cf.max_seqs || dst < 0 || dst >= cf.max_seqs || src == dst)
+    return fail(GQA_ERR_ARG, "bad sequence ids");
+  if (m < 0) return fail(GQA_ERR_ARG, "negative fork length");
+  int32_t src_len = INT32_MAX;
+  for (int l = 0; l < cf.num_layers; ++l) {
+    if (c->len[static_cast<int64_t>(dst) * cf.num_layers + l] != 0)
+      return fail(GQA_ERR_CACHE, "the destination sequence is not empty");
+    src_len = std::min(src_len, c->len[static_cast<int64_t>(src) * cf.num_layers + l]);
+  }
+  if (!c->pages[dst].empty()) return fail(GQA_ERR_CACHE, "the destination sequence is not empty");
+  if (m > src_len) return fail(GQA_ERR_POSITION, "fork length beyond the source's length");
+  const int64_t np = ceil_div(m, kPage);
+  c->pages[dst].assign(c->pages[src].begin(), c->pages[src].begin() + np);
+  for (int64_t lp = 0; lp < np; ++lp) {
+    ++c->ref[c->pages[dst][lp]];
+    c->pending.emplace_back(dst * cf.max_pages_per_seq + static_cast<int32_t>(lp), c->pages[dst][lp]);
+  }
+  for (int l = 0; l < cf.num_layers; ++l) c->len[static_cast<int64_t>(dst) * cf.num_layers + l] = m;
   return GQA_OK;
 }
 
@@ -868,9 +970,6 @@ GQA_EXPORT gqa_status kv_cache_remap(gqa_cache* c, int32_t n, const int32_t* src
   if (n < 0) return fail(GQA_ERR_ARG, "negative page count");
   if (n == 0) return GQA_OK;
   if (!src || !dst) return fail(GQA_ERR_ARG, "src or dst is null");
-  std::vector<int64_t> owner(cf.num_pages, -1);   // seq * max_pages_per_seq + logical page
-  for (int s = 0; s < cf.max_seqs; ++s)
-    for (size_t i = 0; i < c->pages[s].size(); ++i) owner[c->pages[s][i]] = static_cast<int64_t>(s) * cf.max_pages_per_seq + i;
   std::vector<char> is_free(cf.num_pages, 0);
   for (int32_t p : c->free_list) is_free[p] = 1;
   std::vector<char> seen_src(cf.num_pages, 0), seen_dst(cf.num_pages, 0);
@@ -881,34 +980,29 @@ GQA_EXPORT gqa_status kv_cache_remap(gqa_cache* c, int32_t n, const int32_t* src
     seen_src[src[i]] = seen_dst[dst[i]] = 1;
   }
   for (int i = 0; i < n; ++i) {
-    if (owner[src[i]] < 0) return fail(GQA_ERR_CACHE, "source page is not in use");
+    if (c->ref[src[i]] == 0) return fail(GQA_ERR_CACHE, "source page is not in use");
     if (!is_free[dst[i]]) return fail(GQA_ERR_CACHE, "destination page is not free");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   gqa_status st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
-  for (int i0 = 0; i0 < n; i0 += gqa::kMaxPatchPerLaunch) {
-    gqa::CopyArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.k_pool = c->k_pool;
-    a.v_pool = c->v_pool;
-    a.layer_stride = c->layer_elems;
-    a.page_elems = c->page_elems;
-    a.elt_bytes = c->elt;
-    a.n = std::min(n - i0, gqa::kMaxPatchPerLaunch);
-    for (int j = 0; j < a.n; ++j) {
-      a.src[j] = src[i0 + j];
-      a.dst[j] = dst[i0 + j];
+  std::vector<std::pair<int32_t, int32_t>> moves(n);
+  for (int i = 0; i < n; ++i) moves[i] = {src[i], dst[i]};
+  st = launch_copies(c, moves, s);
+  if (st != GQA_OK) return st;
+  // every table entry that references a moved page (a shared page has several)
+  std::vector<int32_t> moved_to(cf.num_pages, -1);
+  for (int i = 0; i < n; ++i) moved_to[src[i]] = dst[i];
+  for (int sq = 0; sq < cf.max_seqs; ++sq)
+    for (size_t lp = 0; lp < c->pages[sq].size(); ++lp) {
+      const int32_t to = moved_to[c->pages[sq][lp]];
+      if (to < 0) continue;
+      c->pages[sq][lp] = to;
+      c->pending.emplace_back(sq * cf.max_pages_per_seq + static_cast<int32_t>(lp), to);
     }
-    hipError_t e = gqa::launch_page_copy(a, cf.num_layers, s);
-    if (e != hipSuccess) return hip_fail(e, "page copy launch");
-  }
   for (int i = 0; i < n; ++i) {
-    const int64_t ow = owner[src[i]];
-    const int sq = static_cast<int>(ow / cf.max_pages_per_seq);
-    const int lp = static_cast<int>(ow % cf.max_pages_per_seq);
-    c->pages[sq][lp] = dst[i];
-    c->pending.emplace_back(sq * cf.max_pages_per_seq + lp, dst[i]);
+    c->ref[dst[i]] = c->ref[src[i]];
+    c->ref[src[i]] = 0;
     c->free_list.erase(std::find(c->free_list.begin(), c->free_list.end(), dst[i]));
   }
   for (int i = 0; i < n; ++i) c->free_list.push_back(src[i]);
@@ -957,11 +1051,20 @@ GQA_EXPORT gqa_status gqa_cache_check(const gqa_cache* c) {
     if (lmin != lmax) return fail(GQA_ERR_CACHE, "sequence " + std::to_string(s) + ": layer lengths differ");
     if (static_cast<int64_t>(c->pages[s].size()) != ceil_div(lmax, kPage))
       return fail(GQA_ERR_CACHE, "sequence " + std::to_string(s) + ": page count does not match its length");
+    std::vector<int32_t> own(c->pages[s]);
+    std::sort(own.begin(), own.end());
+    if (std::adjacent_find(own.begin(), own.end()) != own.end())
+      return fail(GQA_ERR_CACHE, "sequence " + std::to_string(s) + ": a page appears twice in its table");
     for (int32_t p : c->pages[s]) ++count[p];
   }
-  for (int32_t p : c->free_list) ++count[p];
-  for (int p = 0; p < cf.num_pages; ++p)
-    if (count[p] != 1) return fail(GQA_ERR_CACHE, "page " + std::to_string(p) + " is lost or owned twice");
+  std::vector<int> listed(cf.num_pages, 0);
+  for (int32_t p : c->free_list) ++listed[p];
+  for (int p = 0; p < cf.num_pages; ++p) {
+    if (count[p] != c->ref[p])
+      return fail(GQA_ERR_CACHE, "page " + std::to_string(p) + ": reference count differs from the tables");
+    if (listed[p] > 1 || (listed[p] == 1) == (count[p] > 0))
+      return fail(GQA_ERR_CACHE, "page " + std::to_string(p) + " is lost, listed twice or free while referenced");
+  }
   return GQA_OK;
 }
 

@@ -203,17 +203,36 @@ gqa_status gqa_decode_step(gqa_cache* cache, int32_t layer, int32_t B, const int
                            const gqa_tensor* o, void* workspace, size_t ws_bytes, void* stream);
 
 /* Prompt edit at position m ([P3] prompt-edit lesson): keep positions [0,m) in
- * every layer of seq_id, drop the rest and return pages no layer still uses to
+ * every layer of seq_id, drop the rest and give up the sequence's references to
+ * the pages no layer still uses; a page whose last reference goes returns to
  * the back of the free list (ascending logical order).  Host only; no launch.
  * m beyond a layer's length leaves that layer unchanged.  m == 0 releases the
  * sequence. */
 gqa_status kv_cache_truncate(gqa_cache* cache, int32_t seq_id, int32_t m);
 
+/* Prefix sharing ([P3] prefix-sharing lesson: requests whose first m tokens
+ * agree have the same per-layer K/V there, so a second request references the
+ * cached blocks instead of prefilling them again).  Sequence dst, which must
+ * be empty (length 0 in every layer), takes src's positions [0, m) in every
+ * layer: its first ceil(m/16) block-table entries become src's pages, each
+ * counting one more reference.  Nothing is copied.  Later, a write into a page
+ * that more than one table references (the page holding slot m when m is not a
+ * multiple of 16, or any page after a truncate inside it) first copies that
+ * page, every layer, to a page from the front of the free list, and the
+ * writer's entry points at the copy (copy-on-write for a fork inside a block);
+ * the copy runs on the stream of the writing call.  A shared page returns to
+ * the free list only when its last reference goes (truncate).  Host only; no
+ * launch.  Errors: GQA_ERR_ARG (ids out of range, src == dst, m < 0),
+ * GQA_ERR_CACHE (dst not empty), GQA_ERR_POSITION (m beyond src's length in
+ * some layer). */
+gqa_status kv_cache_fork(gqa_cache* cache, int32_t src_seq, int32_t dst_seq, int32_t m);
+
 /* Move n physical pages ([P1] 2.2: the manager may move physical pages but not
  * change which tokens they hold).  src_pages (host) must be in use, dst_pages
  * (host) free and all distinct.  Copies every layer's K and V of each page on
- * `stream`, rewrites the block tables and returns the source pages to the back
- * of the free list in the order given. */
+ * `stream`, rewrites every block-table entry that references a moved page (a
+ * shared page has several) and returns the source pages to the back of the
+ * free list in the order given. */
 gqa_status kv_cache_remap(gqa_cache* cache, int32_t n, const int32_t* src_pages,
                           const int32_t* dst_pages, void* stream);
 
@@ -223,8 +242,10 @@ gqa_status gqa_cache_page_table(const gqa_cache* cache, int32_t seq_id, int32_t*
                                 int32_t* n_out);
 gqa_status gqa_cache_free_pages(const gqa_cache* cache, int32_t* out);
 /* Cache invariants ([P1] 2.5, invariants 2.2): every layer of a sequence has the
- * same length, a sequence owns exactly ceil(length/page_size) pages, and every
- * page is either free or owned by exactly one sequence.  GQA_ERR_CACHE if not. */
+ * same length, a sequence's table holds exactly ceil(length/page_size) distinct
+ * pages, every page's reference count equals the table entries that name it,
+ * and every page is either referenced or listed once in the free list.
+ * GQA_ERR_CACHE if not. */
 gqa_status gqa_cache_check(const gqa_cache* cache);
 
 /* Device workspace bytes that suffice for gqa_decode / gqa_decode_step with up

@@ -108,13 +108,27 @@ class Pair:
         self.lib.kv_cache_truncate(self.gpu.handle, seq, m)
         self.ref.truncate(seq, m)
 
+    def fork(self, src, dst, m):
+        self.lib.kv_cache_fork(self.gpu.handle, src, dst, m)
+        self.ref.fork(src, dst, m)
+
     # ------------------------------------------------------------ checks
-    def check_cache(self, seqs, layers=None):
+    def check_cache(self, seqs, layers=None, invariants=True, device_tables=True):
+        """Block tables, lengths and K/V bytes of the given sequences against the
+        oracle; with ``invariants`` also both sides' cache invariants (every
+        layer of a sequence at the same length) and the free-page count.  Host-only
+        calls (fork, truncate) leave the device block table to the next launch,
+        so right after them ``device_tables=False``."""
         torch.cuda.synchronize()
+        if invariants:
+            self.lib.gqa_cache_check(self.gpu.handle)
+            assert self.ref.check() == []
+        assert self.lib.gqa_cache_free_pages(self.gpu.handle) == len(self.ref.free), "free page count"
         for s in seqs:
             host_table = self.lib.gqa_cache_page_table(self.gpu.handle, s)
             assert host_table == self.ref.page_table(s), f"block table of sequence {s}"
-            assert self.gpu.device_table(s, len(host_table)) == host_table, f"device table of sequence {s}"
+            if device_tables:
+                assert self.gpu.device_table(s, len(host_table)) == host_table, f"device table of sequence {s}"
             for l in (layers if layers is not None else range(self.ref.L)):
                 assert self.lib.gqa_cache_length(self.gpu.handle, s, l) == self.ref.cache_length(s, l)
                 k, v = self.gpu.gather(s, l)

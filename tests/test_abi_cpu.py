@@ -134,6 +134,10 @@ def _bad_calls(lib, h):
         "CACHE": lambda: lib.gqa_decode(h, 0, [0], FakeTensor((1, 4, 1, 64)), [1], FakeTensor((1, 4, 1, 64))),
         "ARG_DUP": lambda: lib.kv_cache_append(h, 0, [0, 0], FakeTensor((2, 2, 3, 64)), FakeTensor((2, 2, 3, 64)),
                                                np.ones((2, 3), np.uint8), np.array([[0, 1, 2]] * 2, np.int32)),
+        "FORK_SELF": lambda: lib.kv_cache_fork(h, 0, 0, 0),
+        "FORK_RANGE": lambda: lib.kv_cache_fork(h, 0, 2, 0),
+        "FORK_NEG": lambda: lib.kv_cache_fork(h, 0, 1, -1),
+        "FORK_LONG": lambda: lib.kv_cache_fork(h, 0, 1, 1),
     }
 
 
@@ -162,6 +166,10 @@ def _oracle_codes():
     run("CACHE", lambda m: m.decode(0, [0], z(1, 4, 1, 64), [1]))
     run("ARG_DUP", lambda m: m.append(0, [0, 0], z(2, 2, 3, 64), z(2, 2, 3, 64), np.ones((2, 3)),
                                       np.array([[0, 1, 2]] * 2)))
+    run("FORK_SELF", lambda m: m.fork(0, 0, 0))
+    run("FORK_RANGE", lambda m: m.fork(0, 2, 0))
+    run("FORK_NEG", lambda m: m.fork(0, 1, -1))
+    run("FORK_LONG", lambda m: m.fork(0, 1, 1))
     return out
 
 
@@ -177,4 +185,8 @@ def test_rejections_match_oracle_without_gpu():
     # nothing changed
     lib.gqa_cache_check(h)
     assert lib.gqa_cache_free_pages(h) == 4 and lib.gqa_cache_length(h, 0, 0) == 0
+    # an empty fork is valid, leaves the destination empty and takes no page
+    lib.kv_cache_fork(h, 0, 1, 0)
+    lib.gqa_cache_check(h)
+    assert lib.gqa_cache_free_pages(h) == 4 and lib.gqa_cache_page_table(h, 1) == []
     lib.gqa_cache_destroy(h)

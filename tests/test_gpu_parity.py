@@ -269,7 +269,7 @@ def _sampled_prefill(shape, inp, order, rows, layers=1, seqs=None):
         ref = pair.ref.prefill_rows(0, b, q_rows, rows)
         _, rel = compare_rows(Oc[b, :, rows, :], ref, shape.dtype)
         worst = max(worst, rel)
-    pair.check_cache(seqs if seqs is not None else ids)
+    pair.check_cache(seqs if seqs is not None else ids, invariants=layers == 1)
     return pair, worst
 
 
