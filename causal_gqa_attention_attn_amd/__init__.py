@@ -34,7 +34,8 @@ STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "MASK", -5: "POSITIO
 EXPORTS = ["gqa_cache_buffer_sizes", "gqa_cache_create", "gqa_cache_destroy", "kv_cache_append",
            "gqa_prefill", "gqa_attention", "gqa_decode", "gqa_decode_step", "kv_cache_truncate", "kv_cache_fork", "kv_cache_remap", "gqa_cache_length",
            "gqa_cache_page_table", "gqa_cache_free_pages", "gqa_cache_check", "gqa_workspace_size",
-           "gqa_attention_workspace_size",
+           "gqa_attention_workspace_size", "gqa_prefix_index_create", "gqa_prefix_index_destroy",
+           "gqa_prefix_index_insert", "gqa_prefix_index_remove", "gqa_prefix_index_match",
            "gqa_last_error"]
 
 
@@ -76,6 +77,11 @@ _sig = {
     "gqa_decode_step": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _TP, _TP, _TP, _P, ctypes.c_size_t, _P],
     "kv_cache_truncate": [_P, ctypes.c_int32, ctypes.c_int32],
     "kv_cache_fork": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
+    "gqa_prefix_index_create": [_P],
+    "gqa_prefix_index_destroy": [_P],
+    "gqa_prefix_index_insert": [_P, ctypes.c_int32, _P, ctypes.c_int32],
+    "gqa_prefix_index_remove": [_P, ctypes.c_int32],
+    "gqa_prefix_index_match": [_P, _P, ctypes.c_int32, _P, _P],
     "kv_cache_remap": [_P, ctypes.c_int32, _P, _P, _P],
     "gqa_cache_length": [_P, ctypes.c_int32, ctypes.c_int32, _I32P],
     "gqa_cache_page_table": [_P, ctypes.c_int32, _P, ctypes.c_int32, _I32P],
@@ -225,6 +231,34 @@ def kv_cache_truncate(handle, seq_id, m):
 
 def kv_cache_fork(handle, src_seq, dst_seq, m):
     _check(_lib.kv_cache_fork(handle, src_seq, dst_seq, m), "kv_cache_fork")
+
+
+class PrefixIndex:
+    """Host radix tree over recorded requests' token ids (gqa_prefix_index_*)."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(_lib.gqa_prefix_index_create(ctypes.byref(h)), "gqa_prefix_index_create")
+        self.handle = h
+
+    def insert(self, seq, tokens):
+        t = _host_i32(tokens)
+        _check(_lib.gqa_prefix_index_insert(self.handle, seq, _ptr(t), t.size), "gqa_prefix_index_insert")
+
+    def remove(self, seq):
+        _check(_lib.gqa_prefix_index_remove(self.handle, seq), "gqa_prefix_index_remove")
+
+    def match(self, tokens):
+        t = _host_i32(tokens)
+        s, m = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.gqa_prefix_index_match(self.handle, _ptr(t), t.size, ctypes.byref(s), ctypes.byref(m)),
+               "gqa_prefix_index_match")
+        return s.value, m.value
+
+    def close(self):
+        if self.handle:
+            _lib.gqa_prefix_index_destroy(self.handle)
+            self.handle = None
 
 
 def kv_cache_remap(handle, src_pages, dst_pages, stream=None):

@@ -1068,4 +1068,9 @@ GQA_EXPORT gqa_status gqa_cache_check(const gqa_cache* c) {
   return GQA_OK;
 }
 
+namespace gqa {
+// for the other host sources of the library (the prefix index)
+void set_last_error(const char* msg) { g_err = msg; }
+}  // namespace gqa
+
 GQA_EXPORT const char* gqa_last_error(void) { return g_err.c_str(); }

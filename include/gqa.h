@@ -227,6 +227,29 @@ gqa_status kv_cache_truncate(gqa_cache* cache, int32_t seq_id, int32_t m);
  * some layer). */
 gqa_status kv_cache_fork(gqa_cache* cache, int32_t src_seq, int32_t dst_seq, int32_t m);
 
+/* Prefix index ([P3] prefix-sharing lesson: a cached prefix is reusable only
+ * on an exact token-id match, and two requests that first differ at index m
+ * share positions 0..m-1; a prefix tree over the requests answers which prefix
+ * is reusable, the block tables where it lives).  A host-only radix tree over
+ * the token ids the caller records per request; it never touches the cache:
+ * the caller keeps it in step with the cache (insert after a prefill, remove
+ * or re-insert after a truncate) and shares the match with kv_cache_fork.
+ * Not thread-safe; no HIP call. */
+typedef struct gqa_prefix_index gqa_prefix_index;
+gqa_status gqa_prefix_index_create(gqa_prefix_index** out);
+gqa_status gqa_prefix_index_destroy(gqa_prefix_index* index);
+/* Record that request seq (>= 0) holds the cache of tokens[0..n) (host int32),
+ * replacing what seq held before.  GQA_ERR_ARG on a null index or tokens,
+ * seq < 0 or n < 0. */
+gqa_status gqa_prefix_index_insert(gqa_prefix_index* index, int32_t seq, const int32_t* tokens, int32_t n);
+/* Forget request seq (no-op if it is not recorded). */
+gqa_status gqa_prefix_index_remove(gqa_prefix_index* index, int32_t seq);
+/* Longest common prefix of tokens[0..n) with any recorded request: *m_out its
+ * length and *seq_out the smallest request id that reaches it, or -1 (and
+ * *m_out 0) when no recorded request shares even the first token. */
+gqa_status gqa_prefix_index_match(const gqa_prefix_index* index, const int32_t* tokens, int32_t n,
+                                  int32_t* seq_out, int32_t* m_out);
+
 /* Move n physical pages ([P1] 2.2: the manager may move physical pages but not
  * change which tokens they hold).  src_pages (host) must be in use, dst_pages
  * (host) free and all distinct.  Copies every layer's K and V of each page on
