@@ -29,6 +29,8 @@ truncates between calls), median and minimum of 5 such batches:
   * speculative verify: a 4- and an 8-token chunk appended to and attended
     over each of those 64 caches (gqa_prefill with a workspace, which takes
     the split-T kernel), beside the same call on the tiled prefill kernel;
+  * shared prompt: one gqa_decode_step of 64 requests forked from one
+    8192-token prompt with 512 tokens of their own (prefix sharing);
   * edit re-prefill: 16 sequences of 4096 tokens, each truncated at a seeded
     m_b and its suffix re-prefilled (gqa_prefill on a non-empty cache);
     flops 2*Hq*d*(n^2 - m_b^2).
@@ -202,6 +204,36 @@ def other_configs(lib, W):
             "tiled_kernel_us_median": round(tmed * 1e3, 1)}
     trunc = None
     cache.close()
+    # shared system prompt: 64 requests forked from one 8192-token prompt, each
+    # with 512 tokens of its own, decoding together; the prompt's pages are
+    # stored once and read by every request
+    P0, OWN = 8192, 512
+    pages = P0 // 16 + Bs * (OWN // 16 + 1) + 8
+    sc = lib.PagedCache(1, sh.Hkv, sh.d, pages, Bs + 1, (P0 + OWN) // 16 + 2, dtype=torch.bfloat16,
+                        rope_theta=sh.theta, max_position=P0 + OWN + 16)
+    kf, vf = W.normal_device((1, sh.Hkv, P0, sh.d), 93000), W.normal_device((1, sh.Hkv, P0, sh.d), 93001)
+    lib.kv_cache_append(sc.handle, 0, [Bs], kf, vf, torch.ones((1, P0), dtype=torch.uint8),
+                        torch.arange(P0, dtype=torch.int32)[None])
+    for b in range(Bs):
+        lib.kv_cache_fork(sc.handle, Bs, b, P0)
+    ko, vo = W.normal_device((Bs, sh.Hkv, OWN, sh.d), 93002), W.normal_device((Bs, sh.Hkv, OWN, sh.d), 93003)
+    lib.kv_cache_append(sc.handle, 0, ids, ko, vo, torch.ones((Bs, OWN), dtype=torch.uint8),
+                        (P0 + torch.arange(OWN, dtype=torch.int32))[None].repeat(Bs, 1))
+    del kf, vf, ko, vo
+    med, mn = _median_ms(lambda: lib.gqa_decode_step(sc.handle, 0, ids, q, k, v, o, ws),
+                         before=lambda: [lib.kv_cache_truncate(sc.handle, b, P0 + OWN) for b in ids])
+    logical = Bs * (P0 + OWN + 1) * 2 * sh.Hkv * sh.d * 2
+    stored = (P0 + Bs * (OWN + 1)) * 2 * sh.Hkv * sh.d * 2
+    res["shared_prompt_decode"] = {
+        "workload": "gqa_decode_step of 64 requests forked from one 8192-token prompt (kv_cache_fork), "
+                    "512 own tokens each, Hq=32 Hkv=8 d=128, one layer",
+        "logical_kv_bytes": logical, "stored_kv_bytes": stored,
+        "logical_gbs": round(logical / (med * 1e-3) / 1e9, 1),
+        "stored_gbs": round(stored / (med * 1e-3) / 1e9, 1),
+        "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1),
+        "note": "the prompt's 32 MiB of pages are read by all 64 requests; after the first the reads "
+                "come from L2 and the 256 MB last-level cache, so the logical rate is not an HBM rate"}
+    sc.close()
     # edit re-prefill
     sh = W.EDIT
     full = W.prefill_inputs(sh, 1006)
