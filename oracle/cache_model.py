@@ -35,7 +35,8 @@ Readings fixed here (the pages leave them open):
 
 * position ids of the valid tokens must be c_b, c_b+1, ..., c_b+n_b-1 where c_b
   is the current cache length (slot = position); anything else is rejected;
-* the valid tokens of a row must be one contiguous run (padding on either side);
+* the valid tokens of a row may sit anywhere in it (padding before, after or
+  between them); in row order they take consecutive positions and slots;
 * pages are shared by all layers of a sequence: the first layer that needs a
   logical page takes it; pages are taken from the front of the free list in
   batch order, then logical-page order; pages freed by truncation go to the
@@ -72,18 +73,14 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
-def valid_run(mask_row) -> tuple:
-    """(start, count) of the single run of ones in a 0/1 row; MASK error otherwise."""
+def valid_rows(mask_row) -> tuple:
+    """(rows, count): the rectangular rows whose entry is 1, in order; MASK error
+    for an entry other than 0 or 1 (section 2.2: G takes values in {0, 1})."""
     row = np.asarray(mask_row)
     if not np.isin(row, (0, 1)).all():
         raise OracleError("MASK", "mask entries must be 0 or 1")
     idx = np.nonzero(row)[0]
-    if idx.size == 0:
-        return 0, 0
-    s, e = int(idx[0]), int(idx[-1]) + 1
-    if e - s != idx.size:
-        raise OracleError("MASK", "valid tokens of a row must be contiguous")
-    return s, int(idx.size)
+    return idx, int(idx.size)
 
 
 class CacheModel:
@@ -181,11 +178,11 @@ class CacheModel:
         positions = np.asarray(positions)
         if mask.shape != (B, n) or positions.shape != (B, n):
             raise OracleError("SHAPE", "mask and positions must be [B, n]")
-        runs = [valid_run(mask[b]) for b in range(B)]
+        runs = [valid_rows(mask[b]) for b in range(B)]
         for b, (s, nb) in enumerate(runs):
             c = self.length[(ids[b], layer)]
             want = np.arange(c, c + nb)
-            if not np.array_equal(positions[b, s:s + nb].astype(np.int64), want):
+            if not np.array_equal(positions[b][s].astype(np.int64), want):
                 raise OracleError("POSITION", "positions must continue the cache: c_b, c_b+1, ...")
             if c + nb > self.max_position:
                 raise OracleError("POSITION", "position beyond the configured range")
@@ -230,9 +227,9 @@ class CacheModel:
             key = (ids[b], layer)
             c = self.length[key]
             pos = np.arange(c, c + nb)
-            k_used = round_to_storage(rotate(np.asarray(K[b, :, s:s + nb, :], np.float32), pos, self.theta),
+            k_used = round_to_storage(rotate(np.asarray(K[b][:, s, :], np.float32), pos, self.theta),
                                       self.dtype)
-            v = np.asarray(V[b, :, s:s + nb, :], dtype=np.float32).copy()
+            v = np.asarray(V[b][:, s, :], dtype=np.float32).copy()
             self.K[key] = np.concatenate([self.K[key], k_used], axis=1)
             self.V[key] = np.concatenate([self.V[key], v], axis=1)
             self.length[key] = c + nb
@@ -266,10 +263,10 @@ class CacheModel:
             if nb == 0:
                 continue
             pos = np.arange(starts[b], starts[b] + nb)
-            q_used = round_to_storage(rotate(np.asarray(Q[b, :, s:s + nb, :], np.float32), pos, self.theta),
+            q_used = round_to_storage(rotate(np.asarray(Q[b][:, s, :], np.float32), pos, self.theta),
                                       self.dtype)
             key = (ids[b], layer)
-            O[b, :, s:s + nb, :] = attention.attend_positions(q_used, pos, self.K[key], self.V[key])
+            O[b][:, s, :] = attention.attend_positions(q_used, pos, self.K[key], self.V[key])
         return O
 
     def prefill_rows(self, layer, seq, q_rows, positions):

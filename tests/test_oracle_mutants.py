@@ -8,14 +8,14 @@ bf16 conversion.  The pins of ``test_oracle_pins`` must fail on each.
 import numpy as np
 import pytest
 
-from oracle import attention, bf16, rope
+from oracle import attention, bf16, cache_model, rope
 from oracle.cache_model import CacheModel, _ceil_div
 import test_oracle_pins as pins
 
 ALL_PINS = [pins.check_worked_example, pins.check_single_key_and_uniform,
             pins.check_against_textbook_sdpa, pins.check_brute_force,
             pins.check_mask_counts, pins.check_bf16_rounding, pins.check_rotation,
-            pins.check_cache_counts, pins.check_prefix_sharing,
+            pins.check_cache_counts, pins.check_prefix_sharing, pins.check_padding_placement_invariance,
             pins.check_fork_then_suffix_equals_full_prefill]
 
 
@@ -23,7 +23,7 @@ def _some_pin_fails():
     for pin in ALL_PINS:
         try:
             pin()
-        except (AssertionError, ValueError):
+        except (AssertionError, ValueError, cache_model.OracleError):
             return True
     return False
 
@@ -111,6 +111,15 @@ def _truncate_ignoring_references(self, seq, m):
         self.free.append(p)
 
 
+def _valid_span(mask_row):
+    """Treats everything from the first to the last valid token as valid (holes included)."""
+    idx = np.nonzero(np.asarray(mask_row))[0]
+    if idx.size == 0:
+        return idx, 0
+    rows = np.arange(idx[0], idx[-1] + 1)
+    return rows, int(rows.size)
+
+
 _fork = CacheModel.fork
 
 
@@ -139,6 +148,7 @@ MUTANTS = {
     "no_copy_on_write": (CacheModel, "_copy_on_write", staticmethod(lambda ref, page: False)),
     "shared_page_freed_on_truncate": (CacheModel, "truncate", _truncate_ignoring_references),
     "fork_whole_pages_only": (CacheModel, "fork", _fork_whole_pages_only),
+    "holes_treated_as_valid": (cache_model, "valid_rows", _valid_span),
 }
 
 

@@ -375,6 +375,47 @@ def check_fork_then_suffix_equals_full_prefill():
     assert m.check() == []
 
 
+def check_padding_placement_invariance():
+    """Section 2.2 (padding never becomes visible history) and section 2.11 (an
+    unmasked padding key makes a sample's result depend on the batch layout):
+    the same valid tokens, right-padded, left-padded or with holes between
+    them, give the same cache and the same outputs on their rows, and zeros on
+    every padding row."""
+    rng = np.random.default_rng(13)
+    Hq, Hkv, d, nv, n = 4, 2, 8, 9, 16
+    Qv = rng.standard_normal((Hq, nv, d)).astype(np.float32)
+    Kv = rng.standard_normal((Hkv, nv, d)).astype(np.float32)
+    Vv = rng.standard_normal((Hkv, nv, d)).astype(np.float32)
+    layouts = [list(range(nv)), list(range(n - nv, n)), [0, 2, 3, 6, 7, 8, 11, 14, 15]]
+    outs, caches = [], []
+    for rows in layouts:
+        Q = rng.standard_normal((1, Hq, n, d)).astype(np.float32) * 50   # padding: any values
+        K = rng.standard_normal((1, Hkv, n, d)).astype(np.float32) * 50
+        V = rng.standard_normal((1, Hkv, n, d)).astype(np.float32) * 50
+        Q[0][:, rows], K[0][:, rows], V[0][:, rows] = Qv, Kv, Vv
+        mask = np.zeros((1, n), np.uint8)
+        mask[0, rows] = 1
+        pos = np.full((1, n), -7, np.int32)
+        pos[0, rows] = np.arange(3, 3 + nv)
+        m = _model(num_kv_heads=Hkv, head_dim=d, rope_theta=1e4)
+        _append(m, 0, [0], [3], [0], rng, Hkv=Hkv, d=d)
+        m.K[(0, 0)][:] = 0.25                                       # the same 3-token prefix everywhere
+        m.V[(0, 0)][:] = -0.5
+        O = m.prefill(0, [0], Q, K, V, mask, pos)
+        pad = np.ones(n, bool)
+        pad[rows] = False
+        assert np.all(O[0][:, pad] == 0.0)
+        outs.append(O[0][:, rows])
+        caches.append((m.keys(0, 0).copy(), m.values(0, 0).copy()))
+    for o, (k, v) in zip(outs[1:], caches[1:]):
+        assert np.array_equal(o, outs[0])
+        assert np.array_equal(k, caches[0][0]) and np.array_equal(v, caches[0][1])
+
+
+def test_padding_placement_invariance():
+    check_padding_placement_invariance()
+
+
 def test_prefix_sharing():
     check_prefix_sharing()
     check_fork_then_suffix_equals_full_prefill()
@@ -406,10 +447,14 @@ def test_failure_table():
         m.append(0, [0], K, K, np.ones((1, 3), np.uint8), np.array([[0, 1, 2]]))
     assert e.value.code == "POSITION"
     assert m.cache_length(0, 0) == 5
-    # holes in the validity mask
+    # validity entries outside {0, 1} (section 2.2)
     with pytest.raises(OracleError) as e:
-        m.append(0, [0], K, K, np.array([[1, 0, 1]], np.uint8), np.array([[5, -1, 6]]))
+        m.append(0, [0], K, K, np.array([[1, 2, 1]], np.uint8), np.array([[5, 6, 7]]))
     assert e.value.code == "MASK"
+    # a hole: the valid tokens still take consecutive positions, so 5, 6 (not 5, 7)
+    with pytest.raises(OracleError) as e:
+        m.append(0, [0], K, K, np.array([[1, 0, 1]], np.uint8), np.array([[5, 6, 7]]))
+    assert e.value.code == "POSITION"
     # Hkv must divide Hq
     m2 = _model(num_kv_heads=2)
     Q = np.zeros((1, 3, 2, 4), np.float32)
