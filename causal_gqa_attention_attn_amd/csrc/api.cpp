@@ -142,26 +142,61 @@ gqa_status check_seqs(const gqa_cache* c, int32_t B, const int32_t* seq_ids) {
   return GQA_OK;
 }
 
-gqa_status valid_run(const uint8_t* m, int64_t n, int64_t* row0, int64_t* count) {
-  int64_t first = -1, last = -1, cnt = 0;
-  for (int64_t i = 0; i < n; ++i) {
-    if (m[i] > 1) return fail(GQA_ERR_MASK, "mask entries must be 0 or 1");
-    if (m[i]) {
-      if (first < 0) first = i;
-      last = i;
-      ++cnt;
+// One launch entry: a run of consecutive valid rows of batch row b.  A row
+// whose valid tokens have holes between them gives one entry per run; a row
+// with none gives one empty entry, which only zeroes its output rows.
+struct Entry {
+  int32_t b;          // batch row: index of Q/K/V/O and of seq_ids
+  int32_t start;      // position of the run's first token
+  int32_t count;      // tokens in the run
+  int32_t row0;       // rectangular row of its first token
+  int32_t zlo, zhi;   // rectangular rows [zlo, zhi) whose padding this entry writes as 0
+};
+
+// Runs of valid rows of every batch row, positions c[b], c[b]+1, ... in row
+// order; count[b] = valid tokens of row b.  GQA_ERR_MASK for entries not 0/1.
+gqa_status mask_entries(const uint8_t* mask, int64_t n, int32_t B, const int32_t* c, std::vector<Entry>* out,
+                        std::vector<int32_t>* count) {
+  out->clear();
+  count->assign(B, 0);
+  for (int b = 0; b < B; ++b) {
+    const uint8_t* m = mask + static_cast<int64_t>(b) * n;
+    const size_t first = out->size();
+    int32_t pos = c[b];
+    for (int64_t i = 0; i < n; ++i) {
+      if (m[i] > 1) return fail(GQA_ERR_MASK, "mask entries must be 0 or 1");
+      if (!m[i]) continue;
+      if (i == 0 || !m[i - 1]) out->push_back(Entry{b, pos, 0, static_cast<int32_t>(i), 0, 0});
+      ++out->back().count;
+      ++pos;
+    }
+    (*count)[b] = pos - c[b];
+    if (out->size() == first) out->push_back(Entry{b, c[b], 0, 0, 0, 0});
+    // padding before run k (after run k-1) belongs to entry k; the last entry also takes the tail
+    for (size_t k = first; k < out->size(); ++k) {
+      Entry& e = (*out)[k];
+      e.zlo = k == first ? 0 : (*out)[k - 1].row0 + (*out)[k - 1].count;
+      e.zhi = k + 1 == out->size() ? static_cast<int32_t>(n) : e.row0 + e.count;
     }
   }
-  if (cnt && last - first + 1 != cnt) return fail(GQA_ERR_MASK, "valid tokens of a row must be contiguous");
-  *row0 = cnt ? first : 0;
-  *count = cnt;
+  return GQA_OK;
+}
+
+// Every entry's positions must be its start, start + 1, ...
+gqa_status check_positions(const std::vector<Entry>& es, const int32_t* positions, int64_t n, const char* what) {
+  for (const Entry& e : es) {
+    const int32_t* p = positions + static_cast<int64_t>(e.b) * n + e.row0;
+    for (int i = 0; i < e.count; ++i)
+      if (p[i] != e.start + i) return fail(GQA_ERR_POSITION, what);
+  }
   return GQA_OK;
 }
 
 struct AppendPlan {
   int64_t n = 0;
-  std::vector<int32_t> row0, count, start, need;
+  std::vector<int32_t> count, start, need;  // per batch row: valid tokens, first position, new pages
   std::vector<uint8_t> cow;                 // the row's first write lands in a shared page: copy it first
+  std::vector<Entry> entries;
 };
 
 // Every check of an append (mask, positions, capacity, page budget).
@@ -177,25 +212,21 @@ gqa_status plan_append(const gqa_cache* c, int32_t layer, int32_t B, const int32
   if (st != GQA_OK) return st;
   if (B > 0 && n > 0 && (!mask || !positions)) return fail(GQA_ERR_ARG, "mask or positions is null");
   plan->n = n;
-  plan->row0.assign(B, 0);
-  plan->count.assign(B, 0);
   plan->start.assign(B, 0);
   plan->need.assign(B, 0);
   plan->cow.assign(B, 0);
-  for (int b = 0; b < B; ++b) {
-    int64_t run0 = 0, cnt = 0;
-    gqa_status sr = valid_run(mask + static_cast<int64_t>(b) * n, n, &run0, &cnt);
-    if (sr != GQA_OK) return sr;
-    plan->row0[b] = static_cast<int32_t>(run0);
-    plan->count[b] = static_cast<int32_t>(cnt);
+  for (int b = 0; b < B; ++b) plan->start[b] = c->len[static_cast<int64_t>(seq_ids[b]) * cf.num_layers + layer];
+  if (n > 0) {
+    st = mask_entries(mask, n, B, plan->start.data(), &plan->entries, &plan->count);
+    if (st != GQA_OK) return st;
+    st = check_positions(plan->entries, positions, n, "positions must continue the cache: c_b, c_b+1, ...");
+    if (st != GQA_OK) return st;
+  } else {
+    plan->count.assign(B, 0);
+    plan->entries.clear();
   }
   for (int b = 0; b < B; ++b) {
-    const int s = seq_ids[b];
-    const int32_t c0 = c->len[static_cast<int64_t>(s) * cf.num_layers + layer];
-    plan->start[b] = c0;
-    const int32_t* p = positions + static_cast<int64_t>(b) * n + plan->row0[b];
-    for (int i = 0; i < plan->count[b]; ++i)
-      if (p[i] != c0 + i) return fail(GQA_ERR_POSITION, "positions must continue the cache: c_b, c_b+1, ...");
+    const int32_t c0 = plan->start[b];
     const int64_t end = static_cast<int64_t>(c0) + plan->count[b];
     if (cf.rope_style == 1 && end > cf.max_position) return fail(GQA_ERR_POSITION, "position beyond max_position");
     if (ceil_div(end, kPage) > cf.max_pages_per_seq)
@@ -329,12 +360,17 @@ T* layer_base(void* pool, const gqa_cache* c, int layer) {
 gqa_status launch_append_all(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* K,
                              const gqa_tensor* V, const AppendPlan& plan, hipStream_t s) {
   const gqa_cache_config& cf = c->cfg;
-  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
-    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+  (void)B;
+  std::vector<Entry> es;
+  for (const Entry& e : plan.entries)
+    if (e.count > 0) es.push_back(e);
+  const int E = static_cast<int>(es.size());
+  for (int e0 = 0; e0 < E; e0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(E - e0, kMaxSeqPerLaunch);
     gqa::AppendArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.K = static_cast<const char*>(K->data) + b0 * K->stride[0] * c->elt;
-    a.V = static_cast<const char*>(V->data) + b0 * V->stride[0] * c->elt;
+    a.K = K->data;
+    a.V = V->data;
     a.k_s0 = K->stride[0]; a.k_s1 = K->stride[1]; a.k_s2 = K->stride[2];
     a.v_s0 = V->stride[0]; a.v_s1 = V->stride[1]; a.v_s2 = V->stride[2];
     a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
@@ -347,17 +383,16 @@ gqa_status launch_append_all(gqa_cache* c, int32_t layer, int32_t B, const int32
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
     int grid_x = 0;
     for (int j = 0; j < nb; ++j) {
-      const int b = b0 + j;
-      a.meta.seq[j] = seq_ids[b];
-      a.meta.start[j] = plan.start[b];
-      a.meta.count[j] = plan.count[b];
-      a.meta.row0[j] = plan.row0[b];
-      a.meta.total[j] = plan.start[b] + plan.count[b];
-      if (plan.count[b] > 0) {
-        const int first = plan.start[b] / kPage;
-        const int last = (plan.start[b] + plan.count[b] - 1) / kPage;
-        grid_x = std::max(grid_x, last - first + 1);
-      }
+      const Entry& e = es[e0 + j];
+      a.meta.seq[j] = seq_ids[e.b];
+      a.meta.brow[j] = e.b;
+      a.meta.start[j] = e.start;
+      a.meta.count[j] = e.count;
+      a.meta.row0[j] = e.row0;
+      a.meta.total[j] = e.start + e.count;
+      const int first = e.start / kPage;
+      const int last = (e.start + e.count - 1) / kPage;
+      grid_x = std::max(grid_x, last - first + 1);
     }
     if (grid_x == 0) continue;
     hipError_t e = gqa::launch_append(a, cf.dtype, grid_x, s);
@@ -368,31 +403,33 @@ gqa_status launch_append_all(gqa_cache* c, int32_t layer, int32_t B, const int32
 
 
 // Short query runs (at most GQA_MAX_CHUNK_TOKENS rectangular rows) of a bf16
-// cache go to the split-T kernel when the caller passes a workspace.
-bool use_split(const gqa_cache* c, int64_t n, const void* workspace) {
-  return c->cfg.dtype == GQA_BF16 && n >= 1 && n <= GQA_MAX_CHUNK_TOKENS && workspace != nullptr;
+// cache go to the split-T kernel when the caller passes a workspace and every
+// row's valid tokens are one run (each run would read its whole prefix again).
+bool use_split(const gqa_cache* c, int64_t n, const void* workspace, int32_t B, const std::vector<Entry>& es) {
+  return c->cfg.dtype == GQA_BF16 && n >= 1 && n <= GQA_MAX_CHUNK_TOKENS && workspace != nullptr &&
+         static_cast<int64_t>(es.size()) == B;
 }
-gqa_status check_split_workspace(const gqa_cache* c, int32_t B, int64_t Hq, int64_t n, const int32_t* start,
-                                 const int32_t* count, void* workspace, size_t ws_bytes);
-gqa_status attend_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* Q,
-                        const gqa_tensor* O, int64_t n, const int32_t* start, const int32_t* count,
-                        const int32_t* row0, void* workspace, size_t ws_bytes, hipStream_t s);
+gqa_status check_split_workspace(const gqa_cache* c, int32_t B, int64_t Hq, int64_t n, const std::vector<Entry>& es,
+                                 void* workspace, size_t ws_bytes);
+gqa_status attend_split(gqa_cache* c, int32_t layer, const int32_t* seq_ids, const gqa_tensor* Q, const gqa_tensor* O,
+                        int64_t n, const std::vector<Entry>& es, void* workspace, size_t ws_bytes, hipStream_t s);
 
-// Causal attention of each row's valid queries (positions start[b].., count[b]
-// of them, from rectangular row row0[b]) against slots [0, position] of the
+// Causal attention of every entry's queries (positions start.., count of them,
+// from rectangular row row0 of batch row b) against slots [0, position] of the
 // layer; total[b] = written length of the sequence in that layer.
-gqa_status launch_attention(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* Q,
-                            const gqa_tensor* O, int64_t n, const int32_t* start, const int32_t* count,
-                            const int32_t* row0, const int32_t* total, hipStream_t s) {
+gqa_status launch_attention(gqa_cache* c, int32_t layer, const int32_t* seq_ids, const gqa_tensor* Q,
+                            const gqa_tensor* O, int64_t n, const std::vector<Entry>& es, const int32_t* total,
+                            hipStream_t s) {
   const gqa_cache_config& cf = c->cfg;
   const int64_t Hq = Q->shape[1];
-  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
-    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+  const int E = static_cast<int>(es.size());
+  for (int e0 = 0; e0 < E; e0 += kMaxSeqPerLaunch) {
+    const int nb = std::min(E - e0, kMaxSeqPerLaunch);
     gqa::AttnArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.Q = static_cast<const char*>(Q->data) + b0 * Q->stride[0] * c->elt;
+    a.Q = Q->data;
     a.q_s0 = Q->stride[0]; a.q_s1 = Q->stride[1]; a.q_s2 = Q->stride[2];
-    a.O = static_cast<char*>(O->data) + b0 * O->stride[0] * c->elt;
+    a.O = O->data;
     a.o_s0 = O->stride[0]; a.o_s1 = O->stride[1]; a.o_s2 = O->stride[2];
     a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
     a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
@@ -408,12 +445,15 @@ gqa_status launch_attention(gqa_cache* c, int32_t layer, int32_t B, const int32_
     a.pool_bytes = static_cast<uint32_t>(c->layer_elems * c->elt);
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
     for (int j = 0; j < nb; ++j) {
-      const int b = b0 + j;
-      a.meta.seq[j] = seq_ids[b];
-      a.meta.start[j] = start[b];
-      a.meta.count[j] = count[b];
-      a.meta.row0[j] = row0[b];
-      a.meta.total[j] = total[b];
+      const Entry& e = es[e0 + j];
+      a.meta.seq[j] = seq_ids[e.b];
+      a.meta.brow[j] = e.b;
+      a.meta.start[j] = e.start;
+      a.meta.count[j] = e.count;
+      a.meta.row0[j] = e.row0;
+      a.meta.total[j] = total[e.b];
+      a.meta.zlo[j] = e.zlo;
+      a.meta.zhi[j] = e.zhi;
     }
     hipError_t e = cf.dtype == GQA_BF16 ? gqa::launch_prefill_bf16(a, s) : gqa::launch_attend_f32(a, s);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -537,9 +577,9 @@ GQA_EXPORT gqa_status gqa_prefill(gqa_cache* c, int32_t layer, int32_t B, const 
   AppendPlan plan;
   st = plan_append(c, layer, B, seq_ids, K, V, valid_mask, positions, &plan);
   if (st != GQA_OK) return st;
-  const bool split = use_split(c, n, workspace);
+  const bool split = use_split(c, n, workspace, B, plan.entries);
   if (split) {
-    st = check_split_workspace(c, B, Hq, n, plan.start.data(), plan.count.data(), workspace, ws_bytes);
+    st = check_split_workspace(c, B, Hq, n, plan.entries, workspace, ws_bytes);
     if (st != GQA_OK) return st;
   }
   commit_append(c, layer, B, seq_ids, plan);
@@ -549,13 +589,10 @@ GQA_EXPORT gqa_status gqa_prefill(gqa_cache* c, int32_t layer, int32_t B, const 
   st = launch_append_all(c, layer, B, seq_ids, K, V, plan, s);
   if (st != GQA_OK) return st;
   if (n == 0) return GQA_OK;
-  if (split)
-    return attend_split(c, layer, B, seq_ids, Q, O, n, plan.start.data(), plan.count.data(), plan.row0.data(),
-                        workspace, ws_bytes, s);
+  if (split) return attend_split(c, layer, seq_ids, Q, O, n, plan.entries, workspace, ws_bytes, s);
   std::vector<int32_t> totals(B);
   for (int b = 0; b < B; ++b) totals[b] = plan.start[b] + plan.count[b];
-  return launch_attention(c, layer, B, seq_ids, Q, O, n, plan.start.data(), plan.count.data(), plan.row0.data(),
-                          totals.data(), s);
+  return launch_attention(c, layer, seq_ids, Q, O, n, plan.entries, totals.data(), s);
 }
 
 GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
@@ -576,35 +613,41 @@ GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, cons
   st = check_tensor(O, "O", cf.dtype, B, Hq, n, cf.head_dim);
   if (st != GQA_OK) return st;
   if (B > 0 && n > 0 && (!valid_mask || !positions)) return fail(GQA_ERR_ARG, "mask or positions is null");
-  std::vector<int32_t> row0(B), count(B), start(B), totals(B);
-  for (int b = 0; b < B; ++b) {
-    int64_t run0 = 0, cnt = 0;
-    st = valid_run(valid_mask + static_cast<int64_t>(b) * n, n, &run0, &cnt);
+  // the first valid token of each row fixes the row's positions: start, start + 1, ...
+  std::vector<int32_t> start(B, 0), count, totals(B);
+  std::vector<Entry> es;
+  if (n > 0) {
+    for (int b = 0; b < B; ++b) {
+      const uint8_t* m = valid_mask + static_cast<int64_t>(b) * n;
+      for (int64_t i = 0; i < n; ++i)
+        if (m[i] == 1) {
+          start[b] = positions[static_cast<int64_t>(b) * n + i];
+          break;
+        }
+    }
+    st = mask_entries(valid_mask, n, B, start.data(), &es, &count);
     if (st != GQA_OK) return st;
-    row0[b] = static_cast<int32_t>(run0);
-    count[b] = static_cast<int32_t>(cnt);
+    st = check_positions(es, positions, n, "query positions must be consecutive");
+    if (st != GQA_OK) return st;
+  } else {
+    count.assign(B, 0);
   }
   for (int b = 0; b < B; ++b) {
     const int32_t have = c->len[static_cast<int64_t>(seq_ids[b]) * cf.num_layers + layer];
-    const int32_t* p = positions + static_cast<int64_t>(b) * n + row0[b];
-    start[b] = count[b] ? p[0] : 0;
-    for (int i = 0; i < count[b]; ++i)
-      if (p[i] != start[b] + i) return fail(GQA_ERR_POSITION, "query positions must be consecutive");
     if (count[b] && (start[b] < 0 || static_cast<int64_t>(start[b]) + count[b] > have))
       return fail(GQA_ERR_POSITION, "query positions must lie inside the cached length");
     totals[b] = have;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (use_split(c, n, workspace)) {
-    st = check_split_workspace(c, B, Hq, n, start.data(), count.data(), workspace, ws_bytes);
+  if (use_split(c, n, workspace, B, es)) {
+    st = check_split_workspace(c, B, Hq, n, es, workspace, ws_bytes);
     if (st != GQA_OK) return st;
-    return attend_split(c, layer, B, seq_ids, Q, O, n, start.data(), count.data(), row0.data(), workspace, ws_bytes,
-                        s);
+    return attend_split(c, layer, seq_ids, Q, O, n, es, workspace, ws_bytes, s);
   }
   st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
   if (n == 0) return GQA_OK;
-  return launch_attention(c, layer, B, seq_ids, Q, O, n, start.data(), count.data(), row0.data(), totals.data(), s);
+  return launch_attention(c, layer, seq_ids, Q, O, n, es, totals.data(), s);
 }
 
 // ------------------------------------------------------------------ decode
@@ -690,14 +733,14 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
     const int nb = std::min(B - b0, kMaxSeqPerLaunch);
     gqa::DecodeArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
+    a.q = q->data;
     a.q_s0 = q->stride[0]; a.q_s1 = q->stride[1]; a.q_s2 = q->stride[2];
-    a.o = static_cast<char*>(o->data) + b0 * o->stride[0] * c->elt;
+    a.o = o->data;
     a.o_s0 = o->stride[0]; a.o_s1 = o->stride[1]; a.o_s2 = o->stride[2];
     if (k_new) {
-      a.k_new = static_cast<const char*>(k_new->data) + b0 * k_new->stride[0] * c->elt;
+      a.k_new = k_new->data;
       a.kn_s0 = k_new->stride[0]; a.kn_s1 = k_new->stride[1];
-      a.v_new = static_cast<const char*>(v_new->data) + b0 * v_new->stride[0] * c->elt;
+      a.v_new = v_new->data;
       a.vn_s0 = v_new->stride[0]; a.vn_s1 = v_new->stride[1];
     }
     a.k_pool = static_cast<char*>(c->k_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
@@ -722,10 +765,13 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
     for (int j = 0; j < nb; ++j) {
       const int b = b0 + j;
       a.meta.seq[j] = seq_ids[b];
+      a.meta.brow[j] = b;
       a.meta.start[j] = start[b];
       a.meta.count[j] = count[b];
       a.meta.row0[j] = row0[b];
       a.meta.total[j] = T[b];
+      a.meta.zlo[j] = 0;
+      a.meta.zhi[j] = n_rect;
       a.split_off[j] = off;
       off += static_cast<int>(split_count(T[b], pps));
     }
@@ -773,10 +819,13 @@ gqa_status launch_decode_f32(gqa_cache* c, int32_t layer, int32_t B, const int32
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
     for (int j = 0; j < nb; ++j) {
       a.meta.seq[j] = seq_ids[b0 + j];
+      a.meta.brow[j] = j;
       a.meta.start[j] = T[b0 + j] - 1;
       a.meta.count[j] = 1;
       a.meta.row0[j] = 0;
       a.meta.total[j] = T[b0 + j];
+      a.meta.zlo[j] = 0;
+      a.meta.zhi[j] = 1;
     }
     hipError_t e = gqa::launch_attend_f32(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -815,35 +864,39 @@ gqa_status check_workspace(const gqa_cache* c, int32_t B, int64_t ncol, const in
 }
 
 // Lengths a split-T call reads: start + count keys; a sequence with no query
-// reads none (its single split only zeroes its rows of O).
-std::vector<int32_t> split_lengths(int32_t B, const int32_t* start, const int32_t* count) {
-  std::vector<int32_t> T(B);
-  for (int b = 0; b < B; ++b) T[b] = count[b] ? start[b] + count[b] : 0;
+// reads none (its single split only zeroes its rows of O).  The split path
+// takes one entry per batch row, in batch order.
+std::vector<int32_t> split_lengths(const std::vector<Entry>& es) {
+  std::vector<int32_t> T(es.size());
+  for (size_t b = 0; b < es.size(); ++b) T[b] = es[b].count ? es[b].start + es[b].count : 0;
   return T;
 }
 
-int64_t split_ncol(const gqa_cache* c, int32_t B, int64_t Hq, const int32_t* count) {
+int64_t split_ncol(const gqa_cache* c, int64_t Hq, const std::vector<Entry>& es) {
   int32_t longest = 1;
-  for (int b = 0; b < B; ++b) longest = std::max(longest, count[b]);
+  for (const Entry& e : es) longest = std::max(longest, e.count);
   return static_cast<int64_t>(longest) * (Hq / c->cfg.num_kv_heads);
 }
 
-gqa_status check_split_workspace(const gqa_cache* c, int32_t B, int64_t Hq, int64_t n, const int32_t* start,
-                                 const int32_t* count, void* workspace, size_t ws_bytes) {
-  const std::vector<int32_t> T = split_lengths(B, start, count);
-  return check_workspace(c, B, split_ncol(c, B, Hq, count), T.data(), workspace, ws_bytes,
+gqa_status check_split_workspace(const gqa_cache* c, int32_t B, int64_t Hq, int64_t n, const std::vector<Entry>& es,
+                                 void* workspace, size_t ws_bytes) {
+  const std::vector<int32_t> T = split_lengths(es);
+  return check_workspace(c, B, split_ncol(c, Hq, es), T.data(), workspace, ws_bytes,
                          gqa_attention_workspace_size(c, B, static_cast<int32_t>(Hq), static_cast<int32_t>(n)));
 }
 
-gqa_status attend_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* Q,
-                        const gqa_tensor* O, int64_t n, const int32_t* start, const int32_t* count,
-                        const int32_t* row0, void* workspace, size_t ws_bytes, hipStream_t s) {
-  const std::vector<int32_t> T = split_lengths(B, start, count);
-  std::vector<int32_t> st0(B);
-  for (int b = 0; b < B; ++b) st0[b] = T[b] - count[b];
-  return launch_split(c, layer, B, seq_ids, Q, O, st0.data(), count, row0, static_cast<int>(n),
-                      static_cast<int>(split_ncol(c, B, Q->shape[1], count)), nullptr, nullptr, workspace, ws_bytes,
-                      s);
+gqa_status attend_split(gqa_cache* c, int32_t layer, const int32_t* seq_ids, const gqa_tensor* Q, const gqa_tensor* O,
+                        int64_t n, const std::vector<Entry>& es, void* workspace, size_t ws_bytes, hipStream_t s) {
+  const std::vector<int32_t> T = split_lengths(es);
+  const int32_t B = static_cast<int32_t>(es.size());
+  std::vector<int32_t> st0(B), count(B), row0(B);
+  for (int b = 0; b < B; ++b) {
+    count[b] = es[b].count;
+    row0[b] = es[b].row0;
+    st0[b] = T[b] - count[b];
+  }
+  return launch_split(c, layer, B, seq_ids, Q, O, st0.data(), count.data(), row0.data(), static_cast<int>(n),
+                      static_cast<int>(split_ncol(c, Q->shape[1], es)), nullptr, nullptr, workspace, ws_bytes, s);
 }
 
 }  // namespace

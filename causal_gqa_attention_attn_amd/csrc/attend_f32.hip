@@ -23,14 +23,16 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
   const int c0 = a.meta.start[b];
   const int nb = a.meta.count[b];
   const int r0 = a.meta.row0[b];
-  float* orow = static_cast<float*>(a.O) + b * a.o_s0 + h * a.o_s1 + static_cast<int64_t>(r) * a.o_s2;
+  const int br = a.meta.brow[b];
+  float* orow = static_cast<float*>(a.O) + br * a.o_s0 + h * a.o_s1 + static_cast<int64_t>(r) * a.o_s2;
   if (r < r0 || r >= r0 + nb) {
-    for (int e = 0; e < d; ++e) orow[e] = 0.f;
+    if (r >= a.meta.zlo[b] && r < a.meta.zhi[b])
+      for (int e = 0; e < d; ++e) orow[e] = 0.f;
     return;
   }
   const int pos = c0 + (r - r0);
   const int g = h / (a.Hq / a.Hkv);
-  const float* qrow = static_cast<const float*>(a.Q) + b * a.q_s0 + h * a.q_s1 + static_cast<int64_t>(r) * a.q_s2;
+  const float* qrow = static_cast<const float*>(a.Q) + br * a.q_s0 + h * a.q_s1 + static_cast<int64_t>(r) * a.q_s2;
   // rotated query, read pairwise from memory: q'[i] = x c - y s, q'[i+d/2] = x s + y c
   float q[DMAX];
   const int half = d / 2;

@@ -53,8 +53,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int64_t phys = a.table[static_cast<int64_t>(seq) * a.table_w + lp];
   T* kp = static_cast<T*>(a.k_pool) + (phys * a.Hkv + g) * (kPage * d);
   T* vp = static_cast<T*>(a.v_pool) + (phys * a.Hkv + g) * (d * kPage);
-  const T* kin = static_cast<const T*>(a.K) + b * a.k_s0 + g * a.k_s1;
-  const T* vin = static_cast<const T*>(a.V) + b * a.v_s0 + g * a.v_s1;
+  const T* kin = static_cast<const T*>(a.K) + a.meta.brow[b] * a.k_s0 + g * a.k_s1;
+  const T* vin = static_cast<const T*>(a.V) + a.meta.brow[b] * a.v_s0 + g * a.v_s1;
 
   // keys: rotate in float32 (pairs i, i + d/2), round to the storage dtype
   for (int e = threadIdx.x; e < nslots * d; e += blockDim.x) {
@@ -109,16 +109,28 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
   if (nb == 0) return;
   const int seq = a.meta.seq[b];
   const int c0 = a.meta.start[b];
-  const int r0 = a.meta.row0[b];
   const int lp = c0 / kPage + static_cast<int>(blockIdx.x);
   const int slot_lo = max(c0, lp * kPage);
-  const int slot_hi = min(c0 + nb, lp * kPage + kPage);
-  if (slot_lo >= slot_hi) return;
+  if (slot_lo >= min(c0 + nb, lp * kPage + kPage)) return;
+  // Runs of one row (padding between its valid tokens) can share a page: the
+  // 16-byte value writes below merge slots, so one workgroup, that of the
+  // first run on the page, writes the page's slots of every run of the row.
+  const int brow = a.meta.brow[b];
+  if (b > 0 && a.meta.brow[b - 1] == brow && (a.meta.start[b - 1] + a.meta.count[b - 1] - 1) / kPage == lp) return;
+  int last = b;
+  while (last + 1 < a.nseq && a.meta.brow[last + 1] == brow && a.meta.start[last + 1] < lp * kPage + kPage) ++last;
+  const int slot_hi = min(a.meta.start[last] + a.meta.count[last], lp * kPage + kPage);
+  // rectangular row of a slot of this page
+  auto src_row = [&](int slot) {
+    int j = b;
+    while (j < last && slot >= a.meta.start[j] + a.meta.count[j]) ++j;
+    return a.meta.row0[j] + slot - a.meta.start[j];
+  };
   const int64_t phys = a.table[static_cast<int64_t>(seq) * a.table_w + lp];
   uint16_t* kp = static_cast<uint16_t*>(a.k_pool) + (phys * a.Hkv + g) * (kPage * D);
   uint16_t* vp = static_cast<uint16_t*>(a.v_pool) + (phys * a.Hkv + g) * (D * kPage);
-  const uint16_t* kin = static_cast<const uint16_t*>(a.K) + b * a.k_s0 + g * a.k_s1;
-  const uint16_t* vin = static_cast<const uint16_t*>(a.V) + b * a.v_s0 + g * a.v_s1;
+  const uint16_t* kin = static_cast<const uint16_t*>(a.K) + a.meta.brow[b] * a.k_s0 + g * a.k_s1;
+  const uint16_t* vin = static_cast<const uint16_t*>(a.V) + a.meta.brow[b] * a.v_s0 + g * a.v_s1;
   const int t = threadIdx.x;
 
   // keys
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
     const int p = t - si * PAIRS;
     const int slot = lp * kPage + si;
     if (slot >= slot_lo && slot < slot_hi) {
-      const uint16_t* row = kin + static_cast<int64_t>(r0 + slot - c0) * a.k_s2;
+      const uint16_t* row = kin + static_cast<int64_t>(src_row(slot)) * a.k_s2;
       const u32x4 wlo = *reinterpret_cast<const u32x4*>(row + 8 * p);
       const u32x4 whi = *reinterpret_cast<const u32x4*>(row + D / 2 + 8 * p);
       u32x4 olo = wlo, ohi = whi;
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
     const int slot = lp * kPage + si;
     if (slot >= slot_lo && slot < slot_hi)
       *reinterpret_cast<u32x4*>(&vt[si][ch * 8]) =
-          *reinterpret_cast<const u32x4*>(vin + static_cast<int64_t>(r0 + slot - c0) * a.v_s2 + ch * 8);
+          *reinterpret_cast<const u32x4*>(vin + static_cast<int64_t>(src_row(slot)) * a.v_s2 + ch * 8);
   }
   __syncthreads();
   for (int e = t; e < D * 2; e += 256) {

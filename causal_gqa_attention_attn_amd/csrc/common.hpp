@@ -13,19 +13,28 @@ constexpr int kMaxPatchPerLaunch = 240;
 constexpr int kMaxSplitDecode = 128;   // splits per sequence in one decode launch
 constexpr int kDecodeMergers = 4;      // splits of a sequence that combine the split records
 
-// Per-sequence metadata of one launch.
-//  start: position of the first valid token of the call (= cache length before
-//         an append, = T-1 for a decode query);
-//  count: valid tokens (queries) of the call;
-//  row0:  rectangular row of the first valid token;
+// Per-entry metadata of one launch (an entry is one run of valid tokens of a
+// sequence, or a whole decode row).
+//  start: position of the entry's first token (the cache length before an
+//         append plus the valid tokens of earlier runs of the row; T-1 for a
+//         decode query);
+//  count: tokens (queries) of the entry;
+//  row0:  rectangular row of its first token;
 //  total: cache length the attention reads (keys at slots >= total are never
 //         valid, whatever the page holds).
+//  brow:  batch row of Q/K/V/O the entry reads and writes (a row whose valid
+//         tokens have holes gives one entry per run of consecutive valid rows);
+//  zlo, zhi: rectangular rows [zlo, zhi) whose padding (rows outside
+//         [row0, row0 + count)) the entry writes as 0.
 struct SeqMeta {
   int32_t seq[kMaxSeqPerLaunch];
+  int32_t brow[kMaxSeqPerLaunch];
   int32_t start[kMaxSeqPerLaunch];
   int32_t count[kMaxSeqPerLaunch];
   int32_t row0[kMaxSeqPerLaunch];
   int32_t total[kMaxSeqPerLaunch];
+  int32_t zlo[kMaxSeqPerLaunch];
+  int32_t zhi[kMaxSeqPerLaunch];
 };
 
 struct PatchArgs {

@@ -89,6 +89,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int start = a.meta.start[b];
   const int cnt = a.meta.count[b];
   const int r0 = a.meta.row0[b];
+  const int br = a.meta.brow[b];           // batch row of q, o and the new token
   const int npages = (T + kPage - 1) / kPage;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(npages, p_begin + a.pages_per_split);
@@ -106,8 +107,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
       const int rem = idx - hh * a.n_rect * (D / 8);
       const int rr = rem / (D / 8);
       const int ch = rem - rr * (D / 8);
-      if (rr < r0 || rr >= r0 + cnt) {
-        uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(g * G + hh) * a.o_s1 +
+      if ((rr < r0 || rr >= r0 + cnt) && rr >= a.meta.zlo[b] && rr < a.meta.zhi[b]) {
+        uint16_t* op = static_cast<uint16_t*>(a.o) + br * a.o_s0 + static_cast<int64_t>(g * G + hh) * a.o_s1 +
                        static_cast<int64_t>(rr) * a.o_s2 + ch * 8;
         *reinterpret_cast<u32x4*>(op) = u32x4{0u, 0u, 0u, 0u};
       }
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   auto out_row = [&](int c) {
     const int col = hcb * 16 + c;
     const int t = col / G;
-    return static_cast<uint16_t*>(a.o) + b * a.o_s0 + static_cast<int64_t>(g * G + col - t * G) * a.o_s1 +
+    return static_cast<uint16_t*>(a.o) + br * a.o_s0 + static_cast<int64_t>(g * G + col - t * G) * a.o_s1 +
            static_cast<int64_t>(r0 + t) * a.o_s2;
   };
 
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   int64_t phys[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) phys[j] = trow[min(p_first + 4 * j, p_end - 1)];
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.q_s0 + static_cast<int64_t>(g * G + hl) * a.q_s1 +
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + br * a.q_s0 + static_cast<int64_t>(g * G + hl) * a.q_s1 +
                          static_cast<int64_t>(r0 + tl) * a.q_s2;
   u32x4 qw[NQ];
 #pragma unroll
@@ -159,8 +160,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   u32x4 kw[NQ];
   uint32_t vw[NDB];
   if (owns_new) {
-    const uint16_t* krow = static_cast<const uint16_t*>(a.k_new) + b * a.kn_s0 + static_cast<int64_t>(g) * a.kn_s1;
-    const uint16_t* vrow = static_cast<const uint16_t*>(a.v_new) + b * a.vn_s0 + static_cast<int64_t>(g) * a.vn_s1;
+    const uint16_t* krow = static_cast<const uint16_t*>(a.k_new) + br * a.kn_s0 + static_cast<int64_t>(g) * a.kn_s1;
+    const uint16_t* vrow = static_cast<const uint16_t*>(a.v_new) + br * a.vn_s0 + static_cast<int64_t>(g) * a.vn_s1;
 #pragma unroll
     for (int c = 0; c < NQ; ++c) kw[c] = *reinterpret_cast<const u32x4*>(krow + c * 32 + grp * 8);
 #pragma unroll

@@ -144,22 +144,24 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   const int nb = a.meta.count[b];
   const int r0 = a.meta.row0[b];
   const int total = a.meta.total[b];
+  const int br = a.meta.brow[b];       // batch row of Q and O
+  const int zlo = a.meta.zlo[b], zhi = a.meta.zhi[b];
   const int h0 = g * G + hc * Gc;      // first query head of this workgroup
 
   // padding rows of this workgroup's rectangular range -> 0 (after every
   // page-table read, so those reads may use the scalar cache)
   auto zero_padding = [&]() {
     const int rlo = tile * Tq;
-    const int rhi = min(a.n_rect, rlo + Tq);
+    const int rhi = min(zhi, rlo + Tq);
     const int per_row = D / 8;
     for (int idx = threadIdx.x; idx < Gc * Tq * per_row; idx += 256) {
       const int hh = idx / (Tq * per_row);
       const int rem = idx - hh * Tq * per_row;
       const int rr = rlo + rem / per_row;
       const int ch = rem % per_row;
-      if (rr < rhi && (rr < r0 || rr >= r0 + nb)) {
+      if (rr >= zlo && rr < rhi && (rr < r0 || rr >= r0 + nb)) {
         const u32x4 z = {0u, 0u, 0u, 0u};
-        uint16_t* op = static_cast<uint16_t*>(a.O) + b * a.o_s0 + static_cast<int64_t>(h0 + hh) * a.o_s1 +
+        uint16_t* op = static_cast<uint16_t*>(a.O) + br * a.o_s0 + static_cast<int64_t>(h0 + hh) * a.o_s1 +
                        static_cast<int64_t>(rr) * a.o_s2 + ch * 8;
         *reinterpret_cast<u32x4*>(op) = z;
       }
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
       // every lane loads a valid row (padding lanes reuse the last valid one
       // and are zeroed), so all query and rotation-table loads issue together
       const int tq = min(rb_t + col, qn - 1);
-      const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.q_s0 + static_cast<int64_t>(rb_h) * a.q_s1 +
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + br * a.q_s0 + static_cast<int64_t>(rb_h) * a.q_s1 +
                              static_cast<int64_t>(r0 + t0 + tq) * a.q_s2;
       u32x4 w[NC];
 #pragma unroll
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
 
   const float inv = 1.f / l_tot;
   if (q_ok) {
-    uint16_t* orow = static_cast<uint16_t*>(a.O) + b * a.o_s0 + static_cast<int64_t>(rb_h) * a.o_s1 +
+    uint16_t* orow = static_cast<uint16_t*>(a.O) + br * a.o_s0 + static_cast<int64_t>(rb_h) * a.o_s1 +
                      static_cast<int64_t>(r0 + t0 + rb_t + col) * a.o_s2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

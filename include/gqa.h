@@ -131,11 +131,12 @@ gqa_status gqa_cache_destroy(gqa_cache* cache);
 
 /* Append the valid tokens of K and V to layer `layer` of sequences seq_ids[0..B)
  * ([P1] 2.6 cache.write_sequence; [P3] decode append, one K/V per token).
- *  valid_mask  host uint8 [B][n], 1 = valid token; the valid tokens of each
- *              row must form one contiguous run (padding on either side).
- *  positions   host int32 [B][n]; for the valid tokens they must be
- *              c_b, c_b+1, ... where c_b is the layer's current length for that
- *              sequence (slot = position).  Padding entries are ignored.
+ *  valid_mask  host uint8 [B][n], 1 = valid token, 0 = padding ([P1] 2.2:
+ *              G in {0,1}); padding may sit before, after or between the valid
+ *              tokens of a row.  GQA_ERR_MASK for any other value.
+ *  positions   host int32 [B][n]; for the valid tokens, in row order, they
+ *              must be c_b, c_b+1, ... where c_b is the layer's current length
+ *              for that sequence (slot = position).  Padding entries are ignored.
  * Keys are rotated (rope_style 1) in float32 and rounded to the cache dtype,
  * values are copied bit-exactly.  Pages are taken from the free list when a
  * layer first needs them: in batch order, then logical page order.
@@ -153,7 +154,8 @@ gqa_status kv_cache_append(gqa_cache* cache, int32_t layer, int32_t B, const int
  * cache dtype; accumulation is float32.
  * workspace may be NULL (ws_bytes 0): the query tiles then run on the tiled
  * kernel.  For a bf16 cache and 1 <= n <= GQA_MAX_CHUNK_TOKENS, a non-NULL
- * workspace sends the attention to the split-T kernel instead (the decode
+ * workspace sends the attention to the split-T kernel instead, unless a row's
+ * valid tokens have padding between them (the decode
  * kernel with one matrix column per (query token, head), split over the cached
  * keys, which suits short chunks on long caches); it must then follow the
  * gqa_decode workspace rule with gqa_attention_workspace_size(cache, B, Hq, n)
@@ -166,9 +168,9 @@ gqa_status gqa_prefill(gqa_cache* cache, int32_t layer, int32_t B, const int32_t
 /* The attention half of gqa_prefill ([P1] 2.6 separates cache.write_sequence
  * from causal_attention): for every valid query token, whose K/V must already
  * be in the cache, at position p, O[b,h,i] attends to slots 0..p of layer
- * `layer`.  The valid tokens of a row must carry consecutive positions
- * p0, p0+1, ... that end at or before the layer's current length; rows of O
- * for padding tokens are written as 0.  gqa_prefill is kv_cache_append
+ * `layer`.  The valid tokens of a row (padding may sit between them) must
+ * carry consecutive positions p0, p0+1, ... in row order that end at or before
+ * the layer's current length; rows of O for padding tokens are written as 0.  gqa_prefill is kv_cache_append
  * followed by this call with p0 = the length before the append.  Same
  * workspace rule as gqa_prefill. */
 gqa_status gqa_attention(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,

@@ -123,7 +123,8 @@ def _bad_calls(lib, h):
     pos = np.array([[0, 1, 2]], np.int32)
     return {
         "POSITION": lambda: lib.kv_cache_append(h, 0, [0], K, K, ones, pos + 1),
-        "MASK": lambda: lib.kv_cache_append(h, 0, [0], K, K, np.array([[1, 0, 1]], np.uint8), pos),
+        "MASK": lambda: lib.kv_cache_append(h, 0, [0], K, K, np.array([[1, 2, 1]], np.uint8), pos),
+        "HOLE_POSITION": lambda: lib.kv_cache_append(h, 0, [0], K, K, np.array([[1, 0, 1]], np.uint8), pos),
         "SHAPE": lambda: lib.kv_cache_append(h, 0, [0], FakeTensor((1, 3, 3, 64)), K, ones, pos),
         "DTYPE": lambda: lib.kv_cache_append(h, 0, [0], FakeTensor((1, 2, 3, 64), torch.float32), K, ones, pos),
         "ARG": lambda: lib.kv_cache_append(h, 2, [0], K, K, ones, pos),
@@ -156,7 +157,8 @@ def _oracle_codes():
             out[name] = e.code
 
     run("POSITION", lambda m: m.append(0, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), ones, pos + 1))
-    run("MASK", lambda m: m.append(0, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), np.array([[1, 0, 1]]), pos))
+    run("MASK", lambda m: m.append(0, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), np.array([[1, 2, 1]]), pos))
+    run("HOLE_POSITION", lambda m: m.append(0, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), np.array([[1, 0, 1]]), pos))
     run("SHAPE", lambda m: m.append(0, [0], z(1, 3, 3, 64), z(1, 2, 3, 64), ones, pos))
     run("DTYPE", lambda m: m.append(0, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), ones, pos, dtype="f32"))
     run("ARG", lambda m: m.append(2, [0], z(1, 2, 3, 64), z(1, 2, 3, 64), ones, pos))
