@@ -31,6 +31,8 @@ truncates between calls), median and minimum of 5 such batches:
     the split-T kernel), beside the same call on the tiled prefill kernel;
   * shared prompt: one gqa_decode_step of 64 requests forked from one
     8192-token prompt with 512 tokens of their own (prefix sharing);
+  * masks with holes: the Llama-shaped prefill with 1536 valid tokens per
+    row in 16 runs separated by padding, beside the same tokens right-padded;
   * edit re-prefill: 16 sequences of 4096 tokens, each truncated at a seeded
     m_b and its suffix re-prefilled (gqa_prefill on a non-empty cache);
     flops 2*Hq*d*(n^2 - m_b^2).
@@ -136,6 +138,7 @@ def _median_ms(fn, before=None, iters=20, warm=3, reps=5):
 
 
 def other_configs(lib, W):
+    import numpy as np
     import torch
     res = {}
     # Llama-shaped prefill
@@ -234,6 +237,45 @@ def other_configs(lib, W):
         "note": "the prompt's 32 MiB of pages are read by all 64 requests; after the first the reads "
                 "come from L2 and the 256 MB last-level cache, so the logical rate is not an HBM rate"}
     sc.close()
+    # masks with holes: 8 rows of 2048 rectangular slots, 1536 valid tokens each in
+    # 16 runs separated by padding, beside the same tokens right-padded
+    sh = W.LLAMA
+    nv, runs = 1536, 16
+    rng = np.random.default_rng(1008)
+    hole_rows = []
+    per_run = nv // runs
+    for b in range(sh.B):
+        # the padding rows: a random leading gap, 15 inner gaps of at least one row, a tail
+        extra = rng.multinomial(sh.n - nv - (runs - 1), [1.0 / (runs + 1)] * (runs + 1))
+        rows, r = [], int(extra[0])
+        for k in range(runs):
+            rows.extend(range(r, r + per_run))
+            r += per_run + (1 + int(extra[k + 1]) if k + 1 < runs else 0)
+        hole_rows.append(rows)
+    inp = W.prefill_inputs(W.AttnShape(B=sh.B, n=sh.n, Hq=sh.Hq, Hkv=sh.Hkv, d=sh.d, dtype=sh.dtype,
+                                       theta=sh.theta), 1008, lengths=[nv] * sh.B)
+    Qh, Kh, Vh = inp.Q.cuda(), inp.K.cuda(), inp.V.cuda()
+    Oh = torch.empty_like(Qh)
+    hm = torch.zeros((sh.B, sh.n), dtype=torch.uint8)
+    hp = torch.full((sh.B, sh.n), -1, dtype=torch.int32)
+    for b, rows in enumerate(hole_rows):
+        hm[b, rows] = 1
+        hp[b, rows] = torch.arange(nv, dtype=torch.int32)
+    pre = lib.PagedCache(1, sh.Hkv, sh.d, sh.B * (sh.n // 16) + 16, sh.B, sh.n // 16 + 2, dtype=torch.bfloat16,
+                         rope_theta=sh.theta, max_position=sh.n + 32)
+    ids = list(range(sh.B))
+    reset = lambda: [lib.kv_cache_truncate(pre.handle, b, 0) for b in ids]
+    med, mn = _median_ms(lambda: lib.gqa_prefill(pre.handle, 0, ids, Qh, Kh, Vh, hm, hp, Oh), before=reset)
+    rmed, _ = _median_ms(lambda: lib.gqa_prefill(pre.handle, 0, ids, Qh, Kh, Vh, inp.mask, inp.positions, Oh),
+                         before=reset)
+    flops = sh.B * 2.0 * sh.Hq * sh.d * nv * nv
+    res["holey_mask_prefill"] = {
+        "workload": "gqa_prefill B=8, 2048 rectangular rows, 1536 valid tokens per row in 16 runs separated "
+                    "by padding, Hq=32 Hkv=8 d=128",
+        "tflops": round(flops / (med * 1e-3) / 1e12, 1), "ms_median": round(med, 4), "ms_min": round(mn, 4),
+        "right_padded_ms_median": round(rmed, 4)}
+    pre.close()
+    del Qh, Kh, Vh, Oh
     # edit re-prefill
     sh = W.EDIT
     full = W.prefill_inputs(sh, 1006)

@@ -69,16 +69,15 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int G = a.Hq / a.Hkv;
   const int hchunks = (a.ncol + 15) >> 4;
   const int gy = a.Hkv * hchunks;          // (kv head, column chunk) rows of the split records
-  // blockIdx.x = (block of 8 consecutive splits, column chunk, split in the
-  // block): the column chunks of one split are 8 workgroups apart, so they
-  // run on the same XCD (workgroup index mod 8) one shortly after another and
-  // the later ones find the split's pages in that XCD's L2.
-  const int xb = blockIdx.x / (8 * hchunks);
-  const int xr = blockIdx.x - xb * 8 * hchunks;
-  const int hcb = xr >> 3;
-  const int gsplit = xb * 8 + (xr & 7);
-  if (gsplit >= a.split_off[a.nseq]) return;   // padding of the last block of 8
-  const int g = blockIdx.y;
+  // blockIdx.x = (split, column chunk, kv head), kv head fastest: the
+  // workgroups running at one time cover every kv head of the same few pages
+  // (whole 32 KiB page rows of the pool), and the column chunks of one (split,
+  // kv head) run Hkv workgroups apart, on the same XCD (workgroup index mod 8)
+  // when Hkv is a multiple of 8, so the later chunks find the pages in its L2.
+  const int g = blockIdx.x % a.Hkv;
+  const int xr = blockIdx.x / a.Hkv;
+  const int hcb = xr % hchunks;
+  const int gsplit = xr / hchunks;
   const int yrow = g * hchunks + hcb;
   int b = 0;
   while (b + 1 < a.nseq && a.split_off[b + 1] <= gsplit) ++b;
@@ -491,7 +490,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s) {
   const int hchunks = (a.ncol + 15) / 16;
-  dim3 grid(((total_splits + 7) / 8) * 8 * hchunks, a.Hkv);
+  dim3 grid(total_splits * hchunks * a.Hkv);
   if (a.d == 128)
     hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(256), 0, s, a);
   else
