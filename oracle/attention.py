@@ -18,6 +18,11 @@ position (incremental prefill, page "KV Cache 与 Prefill/Decode 推理路径",
 multi-turn lesson: the old prefix is wholly visible and the new block is
 lower-triangular).  A query at position p may read the slots j <= p, which is
 the same rule as section 2.2 once slot = position.
+
+Sliding window (page "KV Cache 与 Prefill/Decode 推理路径", sliding-window
+lesson): the visible range is the latest W positions, the current one
+included, so a query at position p reads the slots p - W < j <= p.  W = 0
+means no window.
 """
 import numpy as np
 
@@ -53,6 +58,17 @@ def slot_mask(q_pos, T: int) -> np.ndarray:
     q_pos = np.asarray(q_pos, dtype=np.int64)
     j = np.arange(T, dtype=np.int64)
     return np.where(j[None, :] <= q_pos[:, None], 0.0, NEG_INF)
+
+
+def window_mask(q_pos, T: int, W: int) -> np.ndarray:
+    """M[i, j] = 0 for cache slots q_pos[i] - W < j <= q_pos[i], -inf otherwise
+    (W = 0: every slot j <= q_pos[i]); j < T."""
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    j = np.arange(T, dtype=np.int64)[None, :]
+    visible = j <= q_pos[:, None]
+    if W > 0:
+        visible &= j > q_pos[:, None] - W
+    return np.where(visible, 0.0, NEG_INF)
 
 
 def finite_score_count(M) -> int:
@@ -95,8 +111,9 @@ def attend(q_used, k_used, v, M) -> np.ndarray:
     return O
 
 
-def attend_positions(q_used, q_pos, k_used, v, row_chunk: int = 1024) -> np.ndarray:
-    """O for queries at absolute positions q_pos against cache slots 0..T-1.
+def attend_positions(q_used, q_pos, k_used, v, row_chunk: int = 1024, window: int = 0) -> np.ndarray:
+    """O for queries at absolute positions q_pos against cache slots 0..T-1
+    (only the latest ``window`` of them when window > 0).
 
     Rows are independent, so they are evaluated ``row_chunk`` at a time only to
     bound memory; each row's arithmetic is the same as in ``attend``.
@@ -107,5 +124,6 @@ def attend_positions(q_used, q_pos, k_used, v, row_chunk: int = 1024) -> np.ndar
     out = np.zeros(q_used.shape)
     for r0 in range(0, q_used.shape[1], row_chunk):
         r1 = min(q_used.shape[1], r0 + row_chunk)
-        out[:, r0:r1] = attend(q_used[:, r0:r1], k_used, v, slot_mask(q_pos[r0:r1], T))
+        M = window_mask(q_pos[r0:r1], T, window) if window else slot_mask(q_pos[r0:r1], T)
+        out[:, r0:r1] = attend(q_used[:, r0:r1], k_used, v, M)
     return out

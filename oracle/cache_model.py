@@ -23,6 +23,10 @@ Test infrastructure.  Sources:
     [0, m), drop the rest, and run an incremental prefill on the suffix;
   - decode lessons: a single new token appends one K/V per layer and reads all
     T cached entries, with no future entry to mask;
+  - sliding-window lesson: with a window of W positions (the current one
+    included) a query at position t reads positions t-W+1..t; keys that no
+    query will read again need not be kept, and a ring of fixed capacity holds
+    the latest window;
   - prefix-sharing lesson: requests whose first m token ids agree have equal
     per-layer K/V on positions 0..m-1 and may reference the same cache blocks;
     the system counts the references, and a shared block returns to the free
@@ -42,6 +46,16 @@ Readings fixed here (the pages leave them open):
   batch order, then logical-page order; pages freed by truncation go to the
   back in ascending logical order, remapped source pages in the order given;
 * invalid (padding) query rows produce exact zeros;
+* window W > 0 makes the cache a ring: a sequence's block table has at most
+  R = max_pages_per_seq entries and logical page L lives in entry L mod R, so
+  once the ring is full each new logical page reuses, in place, the page of
+  the logical page R before it.  A call that writes positions [c, c+n) must
+  find every position its queries read, [max(0, c-W+1), c+n), in at most R
+  consecutive logical pages (else OUT_OF_PAGES); R must be at least
+  ceil(W/P) + 1 so that a decode step fits.  Truncation of a ring sequence
+  is supported only to 0 (release) or to at least its length (no change), and
+  a ring sequence cannot be forked (UNSUPPORTED): positions the ring has
+  overwritten cannot come back;
 * a fork (sequence dst takes sequence src's positions [0, m)) makes dst's
   first ceil(m/P) table entries the same physical pages as src's, each page
   counting one more reference; nothing is copied then.  A write into a page
@@ -86,7 +100,7 @@ def valid_rows(mask_row) -> tuple:
 class CacheModel:
     def __init__(self, num_layers, num_kv_heads, head_dim, page_size, num_pages,
                  max_seqs, max_pages_per_seq, dtype="bf16", rope_theta=0.0,
-                 max_position=None, free_order=None):
+                 max_position=None, free_order=None, window=0):
         self.L = num_layers
         self.Hkv = num_kv_heads
         self.d = head_dim
@@ -96,6 +110,9 @@ class CacheModel:
         self.max_pages_per_seq = max_pages_per_seq
         self.dtype = dtype
         self.theta = rope_theta
+        self.window = int(window)
+        if self.window < 0 or (self.window and max_pages_per_seq < _ceil_div(self.window, page_size) + 1):
+            raise OracleError("UNSUPPORTED", "a ring must hold a window plus one page")
         self.max_position = max_position if max_position is not None else max_pages_per_seq * page_size
         order = list(range(num_pages)) if free_order is None else [int(p) for p in free_order]
         if sorted(order) != list(range(num_pages)):
@@ -134,7 +151,7 @@ class CacheModel:
             lens = [self.length[(s, l)] for l in range(self.L)]
             if len(set(lens)) > 1:
                 bad.append(f"sequence {s}: layer lengths differ {lens}")
-            if len(self.pages[s]) != _ceil_div(max(lens), self.P):
+            if len(self.pages[s]) != self._table_entries(max(lens)):
                 bad.append(f"sequence {s}: {len(self.pages[s])} pages for length {max(lens)}")
             if len(set(self.pages[s])) != len(self.pages[s]):
                 bad.append(f"sequence {s}: a page appears twice in its table")
@@ -186,7 +203,11 @@ class CacheModel:
                 raise OracleError("POSITION", "positions must continue the cache: c_b, c_b+1, ...")
             if c + nb > self.max_position:
                 raise OracleError("POSITION", "position beyond the configured range")
-            if _ceil_div(c + nb, self.P) > self.max_pages_per_seq:
+            if self.window:
+                first = max(0, c - self.window + 1)
+                if nb and (c + nb - 1) // self.P - first // self.P + 1 > self.max_pages_per_seq:
+                    raise OracleError("OUT_OF_PAGES", "the window and the new tokens exceed the ring")
+            elif _ceil_div(c + nb, self.P) > self.max_pages_per_seq:
                 raise OracleError("OUT_OF_PAGES", "sequence exceeds its block-table capacity")
         need = []
         ref = list(self.ref)        # references as the rows before this one leave them
@@ -194,13 +215,27 @@ class CacheModel:
             c = self.length[(ids[b], layer)]
             # writing from slot c touches an existing page only when c is inside
             # one; that page is copied first if another table references it
-            cow = nb > 0 and c % self.P != 0 and self._copy_on_write(ref, self.pages[ids[b]][c // self.P])
+            cow = (not self.window and nb > 0 and c % self.P != 0
+                   and self._copy_on_write(ref, self.pages[ids[b]][c // self.P]))
             if cow:
                 ref[self.pages[ids[b]][c // self.P]] -= 1
-            need.append((cow, max(0, _ceil_div(c + nb, self.P) - len(self.pages[ids[b]]))))
+            need.append((cow, max(0, self._table_entries(c + nb) - len(self.pages[ids[b]]))))
         if sum(int(cow) + k for cow, k in need) > len(self.free):
             raise OracleError("OUT_OF_PAGES", "not enough free pages")
         return runs, need
+
+    def _table_entries(self, length) -> int:
+        """Block-table entries a sequence of this length holds: one per logical
+        page, at most R in a ring (page L reuses entry L mod R)."""
+        entries = _ceil_div(length, self.P)
+        return min(entries, self.max_pages_per_seq) if self.window else entries
+
+    def resident_from(self, seq, layer) -> int:
+        """First position a ring still holds (0 without a window)."""
+        n = self.length[(seq, layer)]
+        if not self.window or n == 0:
+            return 0
+        return max(0, ((n - 1) // self.P - self.max_pages_per_seq + 1) * self.P)
 
     @staticmethod
     def _copy_on_write(ref, page) -> bool:
@@ -266,7 +301,7 @@ class CacheModel:
             q_used = round_to_storage(rotate(np.asarray(Q[b][:, s, :], np.float32), pos, self.theta),
                                       self.dtype)
             key = (ids[b], layer)
-            O[b][:, s, :] = attention.attend_positions(q_used, pos, self.K[key], self.V[key])
+            O[b][:, s, :] = attention.attend_positions(q_used, pos, self.K[key], self.V[key], window=self.window)
         return O
 
     def prefill_rows(self, layer, seq, q_rows, positions):
@@ -276,9 +311,11 @@ class CacheModel:
         Used to check sampled outputs of large runs without recomputing all rows.
         """
         pos = np.asarray(positions, dtype=np.int64)
+        if self.window and pos.size and pos.min() - self.window + 1 < self.resident_from(seq, layer):
+            raise OracleError("POSITION", "the window of a query reaches positions the ring no longer holds")
         q_used = round_to_storage(rotate(np.asarray(q_rows, np.float32), pos, self.theta), self.dtype)
         key = (seq, layer)
-        return attention.attend_positions(q_used, pos, self.K[key], self.V[key])
+        return attention.attend_positions(q_used, pos, self.K[key], self.V[key], window=self.window)
 
     def decode(self, layer, seq_ids, q, valid_lengths):
         """One query per sequence at position T-1 over all T cached slots."""
@@ -310,6 +347,8 @@ class CacheModel:
             raise OracleError("ARG", "sequence id out of range")
         if m < 0:
             raise OracleError("ARG", "negative truncation point")
+        if self.window and 0 < m < max(self.length[(seq, l)] for l in range(self.L)):
+            raise OracleError("UNSUPPORTED", "a ring sequence can only be released or left as it is")
         for l in range(self.L):
             key = (seq, l)
             n = min(self.length[key], m)
@@ -331,6 +370,8 @@ class CacheModel:
             raise OracleError("ARG", "bad sequence ids")
         if m < 0:
             raise OracleError("ARG", "negative fork length")
+        if self.window:
+            raise OracleError("UNSUPPORTED", "ring sequences are not forked")
         if self.pages[dst] or any(self.length[(dst, l)] for l in range(self.L)):
             raise OracleError("CACHE", "the destination sequence is not empty")
         if m > min(self.length[(src, l)] for l in range(self.L)):

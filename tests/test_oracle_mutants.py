@@ -16,7 +16,8 @@ ALL_PINS = [pins.check_worked_example, pins.check_single_key_and_uniform,
             pins.check_against_textbook_sdpa, pins.check_brute_force,
             pins.check_mask_counts, pins.check_bf16_rounding, pins.check_rotation,
             pins.check_cache_counts, pins.check_prefix_sharing, pins.check_padding_placement_invariance,
-            pins.check_fork_then_suffix_equals_full_prefill]
+            pins.check_fork_then_suffix_equals_full_prefill, pins.check_sliding_window,
+            pins.check_ring_cache]
 
 
 def _some_pin_fails():
@@ -120,6 +121,13 @@ def _valid_span(mask_row):
     return rows, int(rows.size)
 
 
+def _window_one_too_wide(q_pos, T, W):
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    j = np.arange(T, dtype=np.int64)[None, :]
+    visible = (j <= q_pos[:, None]) & ((j >= q_pos[:, None] - W) if W > 0 else True)
+    return np.where(visible, 0.0, float("-inf"))
+
+
 _fork = CacheModel.fork
 
 
@@ -149,6 +157,8 @@ MUTANTS = {
     "shared_page_freed_on_truncate": (CacheModel, "truncate", _truncate_ignoring_references),
     "fork_whole_pages_only": (CacheModel, "fork", _fork_whole_pages_only),
     "holes_treated_as_valid": (cache_model, "valid_rows", _valid_span),
+    "window_one_too_wide": (attention, "window_mask", _window_one_too_wide),
+    "ring_never_reuses": (CacheModel, "_table_entries", lambda self, length: _ceil_div(length, self.P)),
 }
 
 

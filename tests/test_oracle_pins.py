@@ -412,6 +412,80 @@ def check_padding_placement_invariance():
         assert np.array_equal(k, caches[0][0]) and np.array_equal(v, caches[0][1])
 
 
+def check_sliding_window():
+    """Sliding-window lesson of "KV Cache 与 Prefill/Decode 推理路径": the window
+    holds the latest W positions, the current one included (its W = 4 example:
+    the 4th token reads tokens 1..4).  Pinned by special cases (W >= T is plain
+    causal attention; W = 1 returns the query's own value), by slicing the
+    history instead of masking it, and by pure-Python loops."""
+    import math
+    rng = np.random.default_rng(14)
+    Hq, Hkv, d, T = 4, 2, 8, 12
+    q = rng.standard_normal((Hq, T, d))
+    k = rng.standard_normal((Hkv, T, d))
+    v = rng.standard_normal((Hkv, T, d))
+    pos = np.arange(T)
+    full = attention.attend_positions(q, pos, k, v)
+    assert np.array_equal(attention.attend_positions(q, pos, k, v, window=T), full)
+    own = attention.attend_positions(q, pos, k, v, window=1)
+    for h in range(Hq):
+        assert np.allclose(own[h], v[attention.head_map(h, Hq, Hkv)], rtol=0, atol=1e-15)
+    W = 4
+    win = attention.attend_positions(q, pos, k, v, window=W)
+    for p in range(T):
+        lo = max(0, p - W + 1)
+        sl = attention.attend(q[:, p:p + 1], k[:, lo:p + 1], v[:, lo:p + 1], np.zeros((1, p + 1 - lo)))
+        assert np.allclose(win[:, p:p + 1], sl, rtol=0, atol=1e-12)
+        for h in range(Hq):                          # loops and math.fsum
+            g = (h * Hkv) // Hq
+            sc = [math.fsum(q[h, p, e] * k[g, j, e] for e in range(d)) / math.sqrt(d) for j in range(lo, p + 1)]
+            mx = max(sc)
+            ex = [math.exp(x - mx) for x in sc]
+            z = math.fsum(ex)
+            for e in range(d):
+                o = math.fsum(ex[i] * v[g, lo + i, e] for i in range(len(ex))) / z
+                assert abs(o - win[h, p, e]) <= 1e-12
+
+
+def check_ring_cache():
+    """Ring of R pages for a window W: logical page L in entry L mod R, reused in
+    place once the ring is full; a call whose window and new tokens need more
+    than R pages is refused; a ring sequence is only released or kept."""
+    rng = np.random.default_rng(15)
+    m = _model(num_pages=8, max_pages_per_seq=3, window=20, max_position=256)
+    _append(m, 0, [0], [48], [0], rng)
+    assert m.page_table(0) == [0, 1, 2] and len(m.free) == 5
+    _append(m, 0, [0], [1], [48], rng)              # logical page 3 reuses entry 0 (page 0)
+    assert m.page_table(0) == [0, 1, 2] and len(m.free) == 5
+    assert m.resident_from(0, 0) == 16
+    with pytest.raises(OracleError) as e:            # keys 30..88 span logical pages 1..5
+        _append(m, 0, [0], [40], [49], rng)
+    assert e.value.code == "OUT_OF_PAGES"
+    _append(m, 0, [0], [14], [49], rng)
+    assert m.check() == [] and m.cache_length(0, 0) == 63
+    with pytest.raises(OracleError) as e:
+        m.truncate(0, 50)
+    assert e.value.code == "UNSUPPORTED"
+    with pytest.raises(OracleError) as e:
+        m.fork(0, 1, 10)
+    assert e.value.code == "UNSUPPORTED"
+    assert m.resident_from(0, 0) == 16                # logical pages 1..3 remain
+    with pytest.raises(OracleError) as e:            # position 30's window starts at 11 < 16
+        m.prefill_rows(0, 0, np.zeros((1, 1, 4), np.float32), [30])
+    assert e.value.code == "POSITION"
+    m.prefill_rows(0, 0, np.zeros((1, 1, 4), np.float32), [35])
+    m.truncate(0, 0)
+    assert m.page_table(0) == [] and list(m.free)[-3:] == [0, 1, 2] and m.check() == []
+    with pytest.raises(OracleError) as e:
+        _model(max_pages_per_seq=2, window=20)        # a window of 20 may span 3 pages
+    assert e.value.code == "UNSUPPORTED"
+
+
+def test_sliding_window():
+    check_sliding_window()
+    check_ring_cache()
+
+
 def test_padding_placement_invariance():
     check_padding_placement_invariance()
 
