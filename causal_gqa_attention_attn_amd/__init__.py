@@ -57,7 +57,7 @@ class gqa_cache_config(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("rope_style", ctypes.c_int32), ("max_position", ctypes.c_int32),
-                ("rope_theta", ctypes.c_double)]
+                ("rope_theta", ctypes.c_double), ("window", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -312,14 +312,14 @@ class PagedCache:
 
     def __init__(self, num_layers, num_kv_heads, head_dim, num_pages, max_seqs, max_pages_per_seq,
                  dtype=torch.bfloat16, rope_theta=0.0, max_position=None, free_list_order=None,
-                 device="cuda", page_size=16):
+                 device="cuda", page_size=16, window=0):
         self.dtype = dtype
         self.cfg = _cfg(num_layers=num_layers, num_kv_heads=num_kv_heads, head_dim=head_dim,
                         page_size=page_size, num_pages=num_pages, max_seqs=max_seqs,
                         max_pages_per_seq=max_pages_per_seq, dtype=_dtype_code(dtype),
                         rope_style=1 if rope_theta else 0,
                         max_position=max_position if max_position else max_pages_per_seq * page_size,
-                        rope_theta=float(rope_theta))
+                        rope_theta=float(rope_theta), window=int(window))
         kb, vb, tb, rb = gqa_cache_buffer_sizes(self.cfg)
         elt = 2 if dtype == torch.bfloat16 else 4
         self.k_pool = torch.empty(kb // elt, dtype=dtype, device=device)
@@ -330,6 +330,7 @@ class PagedCache:
                                        self.rope_table, free_list_order)
         self.L, self.Hkv, self.d, self.P = num_layers, num_kv_heads, head_dim, page_size
         self.num_pages, self.max_pages_per_seq = num_pages, max_pages_per_seq
+        self.window = int(window)
 
     def close(self):
         if self.handle is not None:
@@ -363,6 +364,29 @@ class PagedCache:
         k = k.permute(1, 0, 2, 3).reshape(self.Hkv, -1, self.d)[:, :n]
         v = v.permute(1, 0, 3, 2).reshape(self.Hkv, -1, self.d)[:, :n]
         return k.cpu(), v.cpu()
+
+    def gather_resident(self, seq_id, layer):
+        """(first, K_used, V) of the positions [first, len) a ring still holds
+        (first = 0 without a window): logical page L is read from table entry
+        L mod max_pages_per_seq."""
+        n = gqa_cache_length(self.handle, seq_id, layer)
+        if not self.window:
+            return (0,) + self.gather(seq_id, layer)
+        if n == 0:
+            z = torch.zeros(self.Hkv, 0, self.d, dtype=self.dtype)
+            return 0, z, z.clone()
+        R = self.max_pages_per_seq
+        pages = gqa_cache_page_table(self.handle, seq_id)
+        last = (n - 1) // self.P
+        first_page = max(0, last - R + 1)
+        idx = torch.tensor([pages[L % R] for L in range(first_page, last + 1)], dtype=torch.long,
+                           device=self.k_pool.device)
+        k = self.k_view()[layer].index_select(0, idx)
+        v = self.v_view()[layer].index_select(0, idx)
+        first = first_page * self.P
+        k = k.permute(1, 0, 2, 3).reshape(self.Hkv, -1, self.d)[:, :n - first]
+        v = v.permute(1, 0, 3, 2).reshape(self.Hkv, -1, self.d)[:, :n - first]
+        return first, k.cpu(), v.cpu()
 
     def device_table(self, seq_id, count):
         return self.page_table.view(-1, self.max_pages_per_seq)[seq_id, :count].cpu().tolist()

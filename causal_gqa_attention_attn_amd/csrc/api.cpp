@@ -101,7 +101,23 @@ gqa_status check_config(const gqa_cache_config* c) {
     if (c->max_position < 1) return fail(GQA_ERR_ARG, "max_position must be >= 1");
     if (!(c->rope_theta > 0.0)) return fail(GQA_ERR_ARG, "rope_theta must be > 0");
   }
+  if (c->window < 0) return fail(GQA_ERR_ARG, "window must be >= 0");
+  if (c->window > 0 && c->max_pages_per_seq < ceil_div(c->window, kPage) + 1)
+    return fail(GQA_ERR_UNSUPPORTED, "a ring must hold a window plus one page");
   return GQA_OK;
+}
+
+// Block-table entries a sequence of this length holds: one per logical page,
+// at most the table width in a ring (logical page L lives in entry L mod R).
+int64_t table_entries(const gqa_cache_config& cf, int64_t length) {
+  const int64_t e = ceil_div(length, kPage);
+  return cf.window ? std::min<int64_t>(e, cf.max_pages_per_seq) : e;
+}
+
+// First position a ring still holds (0 without a window).
+int32_t resident_from(const gqa_cache_config& cf, int32_t length) {
+  if (!cf.window || length == 0) return 0;
+  return std::max(0, ((length - 1) / kPage - cf.max_pages_per_seq + 1) * kPage);
 }
 
 // Strided 4-D tensor of the cache dtype with the given logical shape.
@@ -229,15 +245,21 @@ gqa_status plan_append(const gqa_cache* c, int32_t layer, int32_t B, const int32
     const int32_t c0 = plan->start[b];
     const int64_t end = static_cast<int64_t>(c0) + plan->count[b];
     if (cf.rope_style == 1 && end > cf.max_position) return fail(GQA_ERR_POSITION, "position beyond max_position");
-    if (ceil_div(end, kPage) > cf.max_pages_per_seq)
+    if (cf.window) {
+      // every position the call's queries read, and its writes, at once in the ring
+      const int64_t first = std::max<int64_t>(0, c0 - cf.window + 1);
+      if (plan->count[b] && (end - 1) / kPage - first / kPage + 1 > cf.max_pages_per_seq)
+        return fail(GQA_ERR_OUT_OF_PAGES, "the window and the new tokens exceed the ring");
+    } else if (ceil_div(end, kPage) > cf.max_pages_per_seq) {
       return fail(GQA_ERR_OUT_OF_PAGES, "sequence exceeds its block-table capacity");
+    }
   }
   int64_t total_need = 0;
   std::vector<int32_t> released;            // shared pages that earlier rows of this call copy away from
   for (int b = 0; b < B; ++b) {
     const int s = seq_ids[b];
     const int32_t c0 = plan->start[b];
-    if (plan->count[b] > 0 && c0 % kPage != 0) {
+    if (!cf.window && plan->count[b] > 0 && c0 % kPage != 0) {
       const int32_t page = c->pages[s][c0 / kPage];
       const int32_t refs = c->ref[page] - static_cast<int32_t>(std::count(released.begin(), released.end(), page));
       if (refs > 1) {
@@ -248,7 +270,7 @@ gqa_status plan_append(const gqa_cache* c, int32_t layer, int32_t B, const int32
     }
     const int64_t end = static_cast<int64_t>(c0) + plan->count[b];
     const int64_t have = static_cast<int64_t>(c->pages[s].size());
-    plan->need[b] = static_cast<int32_t>(std::max<int64_t>(0, ceil_div(end, kPage) - have));
+    plan->need[b] = static_cast<int32_t>(std::max<int64_t>(0, table_entries(cf, end) - have));
     total_need += plan->need[b];
   }
   if (total_need > static_cast<int64_t>(c->free_list.size())) return fail(GQA_ERR_OUT_OF_PAGES, "not enough free pages");
@@ -377,6 +399,7 @@ gqa_status launch_append_all(gqa_cache* c, int32_t layer, int32_t B, const int32
     a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
     a.table = c->d_table;
     a.table_w = cf.max_pages_per_seq;
+    a.window = cf.window;
     a.Hkv = cf.num_kv_heads;
     a.d = cf.head_dim;
     a.nseq = nb;
@@ -435,6 +458,7 @@ gqa_status launch_attention(gqa_cache* c, int32_t layer, const int32_t* seq_ids,
     a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
     a.table = c->d_table;
     a.table_w = cf.max_pages_per_seq;
+    a.window = cf.window;
     a.Hq = static_cast<int32_t>(Hq);
     a.Hkv = cf.num_kv_heads;
     a.d = cf.head_dim;
@@ -636,6 +660,8 @@ GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, cons
     const int32_t have = c->len[static_cast<int64_t>(seq_ids[b]) * cf.num_layers + layer];
     if (count[b] && (start[b] < 0 || static_cast<int64_t>(start[b]) + count[b] > have))
       return fail(GQA_ERR_POSITION, "query positions must lie inside the cached length");
+    if (count[b] && start[b] - cf.window + 1 < resident_from(cf, have))
+      return fail(GQA_ERR_POSITION, "the window of a query reaches positions the ring no longer holds");
     totals[b] = have;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -697,8 +723,17 @@ int decode_pages_per_split(const int32_t* T, int B, int64_t ys) {
   return static_cast<int>(pps);
 }
 
-// Splits of a sequence of T keys (one at least, so that a sequence with no
-// query still gets the workgroup that zeroes its padding rows).
+// Keys a split-T entry reads, counted from the first page it reads: with a
+// window, the pages wholly before its first query's window are skipped.
+int32_t read_length(const gqa_cache* c, int32_t start, int32_t count) {
+  if (count == 0) return 0;
+  const int32_t T = start + count;
+  if (!c->cfg.window) return T;
+  return T - (std::max(0, start - c->cfg.window + 1) / kPage) * kPage;
+}
+
+// Splits of an entry that reads T keys (one at least, so that a sequence with
+// no query still gets the workgroup that zeroes its padding rows).
 int64_t split_count(int32_t T, int pps) { return std::max<int64_t>(1, ceil_div(ceil_div(T, kPage), pps)); }
 
 // Workspace bytes that suffice for B sequences at ys grid rows, whatever the
@@ -722,9 +757,12 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
   const gqa_cache_config& cf = c->cfg;
   const int64_t Hq = q->shape[1];
   const int64_t ys = split_ys(c, ncol);
-  std::vector<int32_t> T(B);
-  for (int b = 0; b < B; ++b) T[b] = start[b] + count[b];
-  const int pps = decode_pages_per_split(T.data(), B, ys);
+  std::vector<int32_t> T(B), Tr(B);
+  for (int b = 0; b < B; ++b) {
+    T[b] = start[b] + count[b];
+    Tr[b] = read_length(c, start[b], count[b]);
+  }
+  const int pps = decode_pages_per_split(Tr.data(), B, ys);
   const WsView wv = ws_view(workspace, ws_bytes, cf.head_dim);
   gqa_status st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
@@ -747,6 +785,7 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
     a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
     a.table = c->d_table;
     a.table_w = cf.max_pages_per_seq;
+    a.window = cf.window;
     a.Hq = static_cast<int32_t>(Hq);
     a.Hkv = cf.num_kv_heads;
     a.d = cf.head_dim;
@@ -773,7 +812,7 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
       a.meta.zlo[j] = 0;
       a.meta.zhi[j] = n_rect;
       a.split_off[j] = off;
-      off += static_cast<int>(split_count(T[b], pps));
+      off += static_cast<int>(split_count(Tr[b], pps));
     }
     a.split_off[nb] = off;
     hipError_t e = gqa::launch_decode_bf16(a, off, s);
@@ -810,6 +849,7 @@ gqa_status launch_decode_f32(gqa_cache* c, int32_t layer, int32_t B, const int32
     a.v_pool = static_cast<char*>(c->v_pool) + static_cast<int64_t>(layer) * c->layer_elems * c->elt;
     a.table = c->d_table;
     a.table_w = cf.max_pages_per_seq;
+    a.window = cf.window;
     a.Hq = static_cast<int32_t>(q->shape[1]);
     a.Hkv = cf.num_kv_heads;
     a.d = cf.head_dim;
@@ -872,6 +912,19 @@ std::vector<int32_t> split_lengths(const std::vector<Entry>& es) {
   return T;
 }
 
+std::vector<int32_t> split_read_lengths(const gqa_cache* c, const std::vector<Entry>& es) {
+  std::vector<int32_t> T(es.size());
+  for (size_t b = 0; b < es.size(); ++b) T[b] = read_length(c, es[b].start, es[b].count);
+  return T;
+}
+
+// read lengths of decode queries at T[b] - 1
+std::vector<int32_t> decode_read_lengths(const gqa_cache* c, int32_t B, const int32_t* T) {
+  std::vector<int32_t> r(B);
+  for (int b = 0; b < B; ++b) r[b] = read_length(c, T[b] - 1, 1);
+  return r;
+}
+
 int64_t split_ncol(const gqa_cache* c, int64_t Hq, const std::vector<Entry>& es) {
   int32_t longest = 1;
   for (const Entry& e : es) longest = std::max(longest, e.count);
@@ -880,7 +933,7 @@ int64_t split_ncol(const gqa_cache* c, int64_t Hq, const std::vector<Entry>& es)
 
 gqa_status check_split_workspace(const gqa_cache* c, int32_t B, int64_t Hq, int64_t n, const std::vector<Entry>& es,
                                  void* workspace, size_t ws_bytes) {
-  const std::vector<int32_t> T = split_lengths(es);
+  const std::vector<int32_t> T = split_read_lengths(c, es);
   return check_workspace(c, B, split_ncol(c, Hq, es), T.data(), workspace, ws_bytes,
                          gqa_attention_workspace_size(c, B, static_cast<int32_t>(Hq), static_cast<int32_t>(n)));
 }
@@ -928,7 +981,8 @@ GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const i
     if (have < 1) return fail(GQA_ERR_CACHE, "decode needs at least one cached token");
   }
   if (B == 0) return GQA_OK;
-  st = check_workspace(c, B, q->shape[1] / cf.num_kv_heads, valid_lengths, workspace, ws_bytes,
+  st = check_workspace(c, B, q->shape[1] / cf.num_kv_heads, decode_read_lengths(c, B, valid_lengths).data(),
+                       workspace, ws_bytes,
                        gqa_workspace_size(c, B, static_cast<int32_t>(q->shape[1])));
   if (st != GQA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -957,7 +1011,8 @@ GQA_EXPORT gqa_status gqa_decode_step(gqa_cache* c, int32_t layer, int32_t B, co
   if (plan.n != 1) return fail(GQA_ERR_SHAPE, "k_new and v_new must hold one token: [B, Hkv, 1, d]");
   std::vector<int32_t> T(B);
   for (int b = 0; b < B; ++b) T[b] = pos[b] + 1;
-  st = check_workspace(c, B, q->shape[1] / cf.num_kv_heads, T.data(), workspace, ws_bytes,
+  st = check_workspace(c, B, q->shape[1] / cf.num_kv_heads, decode_read_lengths(c, B, T.data()).data(),
+                       workspace, ws_bytes,
                        gqa_workspace_size(c, B, static_cast<int32_t>(q->shape[1])));
   if (st != GQA_OK) return st;
   commit_append(c, layer, B, seq_ids, plan);
@@ -979,13 +1034,18 @@ GQA_EXPORT gqa_status kv_cache_truncate(gqa_cache* c, int32_t seq_id, int32_t m)
   const gqa_cache_config& cf = c->cfg;
   if (seq_id < 0 || seq_id >= cf.max_seqs) return fail(GQA_ERR_ARG, "sequence id out of range");
   if (m < 0) return fail(GQA_ERR_ARG, "negative truncation point");
+  if (cf.window && m > 0) {
+    for (int l = 0; l < cf.num_layers; ++l)
+      if (m < c->len[static_cast<int64_t>(seq_id) * cf.num_layers + l])
+        return fail(GQA_ERR_UNSUPPORTED, "a ring sequence can only be released or left as it is");
+  }
   int32_t longest = 0;
   for (int l = 0; l < cf.num_layers; ++l) {
     int32_t& n = c->len[static_cast<int64_t>(seq_id) * cf.num_layers + l];
     n = std::min(n, m);
     longest = std::max(longest, n);
   }
-  const size_t keep = static_cast<size_t>(ceil_div(longest, kPage));
+  const size_t keep = static_cast<size_t>(table_entries(cf, longest));
   std::vector<int32_t>& pl = c->pages[seq_id];
   for (size_t i = keep; i < pl.size(); ++i)
     if (--c->ref[pl[i]] == 0) c->free_list.push_back(pl[i]);
@@ -999,6 +1059,7 @@ GQA_EXPORT gqa_status kv_cache_fork(gqa_cache* c, int32_t src, int32_t dst, int3
   if (src < 0 || src >= cf.max_seqs || dst < 0 || dst >= cf.max_seqs || src == dst)
     return fail(GQA_ERR_ARG, "bad sequence ids");
   if (m < 0) return fail(GQA_ERR_ARG, "negative fork length");
+  if (cf.window) return fail(GQA_ERR_UNSUPPORTED, "ring sequences are not forked");
   int32_t src_len = INT32_MAX;
   for (int l = 0; l < cf.num_layers; ++l) {
     if (c->len[static_cast<int64_t>(dst) * cf.num_layers + l] != 0)
@@ -1102,7 +1163,7 @@ GQA_EXPORT gqa_status gqa_cache_check(const gqa_cache* c) {
       lmax = std::max(lmax, n);
     }
     if (lmin != lmax) return fail(GQA_ERR_CACHE, "sequence " + std::to_string(s) + ": layer lengths differ");
-    if (static_cast<int64_t>(c->pages[s].size()) != ceil_div(lmax, kPage))
+    if (static_cast<int64_t>(c->pages[s].size()) != table_entries(cf, lmax))
       return fail(GQA_ERR_CACHE, "sequence " + std::to_string(s) + ": page count does not match its length");
     std::vector<int32_t> own(c->pages[s]);
     std::sort(own.begin(), own.end());

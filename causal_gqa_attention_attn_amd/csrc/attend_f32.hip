@@ -61,8 +61,8 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
   for (int e = 0; e < DMAX; ++e) acc[e] = 0.f;
   float m = -INFINITY;
   float l = 0.f;
-  for (int j = 0; j <= pos; ++j) {
-    const int64_t phys = trow[j / kPage];
+  for (int j = a.window ? max(0, pos - a.window + 1) : 0; j <= pos; ++j) {
+    const int64_t phys = trow[a.window ? (j / kPage) % a.table_w : j / kPage];
     const float* krow = kpool + ((phys * a.Hkv + g) * kPage + (j % kPage)) * d;
     const float* vcol = vpool + (phys * a.Hkv + g) * d * kPage + (j % kPage);
     float s = 0.f;

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int nslots = slot_hi - slot_lo;
   const int d = a.d;
   const int half = d / 2;
-  const int64_t phys = a.table[static_cast<int64_t>(seq) * a.table_w + lp];
+  const int64_t phys = a.table[static_cast<int64_t>(seq) * a.table_w + (a.window ? lp % a.table_w : lp)];
   T* kp = static_cast<T*>(a.k_pool) + (phys * a.Hkv + g) * (kPage * d);
   T* vp = static_cast<T*>(a.v_pool) + (phys * a.Hkv + g) * (d * kPage);
   const T* kin = static_cast<const T*>(a.K) + a.meta.brow[b] * a.k_s0 + g * a.k_s1;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(AppendArgs a) {
     while (j < last && slot >= a.meta.start[j] + a.meta.count[j]) ++j;
     return a.meta.row0[j] + slot - a.meta.start[j];
   };
-  const int64_t phys = a.table[static_cast<int64_t>(seq) * a.table_w + lp];
+  const int64_t phys = a.table[static_cast<int64_t>(seq) * a.table_w + (a.window ? lp % a.table_w : lp)];
   uint16_t* kp = static_cast<uint16_t*>(a.k_pool) + (phys * a.Hkv + g) * (kPage * D);
   uint16_t* vp = static_cast<uint16_t*>(a.v_pool) + (phys * a.Hkv + g) * (D * kPage);
   const uint16_t* kin = static_cast<const uint16_t*>(a.K) + a.meta.brow[b] * a.k_s0 + g * a.k_s1;

@@ -53,6 +53,7 @@ struct AppendArgs {
   void* v_pool;
   const int32_t* table;
   int32_t table_w;
+  int32_t window;             // sliding window (0: none); a windowed cache is a ring of table_w pages
   int32_t Hkv, d, nseq;
   const float* rope;          // [max_position][d/2][2] or nullptr
   SeqMeta meta;
@@ -67,6 +68,7 @@ struct AttnArgs {
   const void* v_pool;
   const int32_t* table;
   int32_t table_w;
+  int32_t window;             // sliding window (0: none); a windowed cache is a ring of table_w pages
   int32_t Hq, Hkv, d, n_rect, nseq;
   float scale;                // 1/sqrt(d)
   float scale_log2;           // log2(e)/sqrt(d)
@@ -88,6 +90,7 @@ struct DecodeArgs {
   void* v_pool;
   const int32_t* table;
   int32_t table_w;
+  int32_t window;             // sliding window (0: none); a windowed cache is a ring of table_w pages
   int32_t Hq, Hkv, d, nseq;
   int32_t ncol;               // (token, head) columns per kv head: tokens of the longest chunk x Hq/Hkv
   int32_t n_rect;             // rows of the rectangular q / o (padding rows of o are zeroed)

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int r0 = a.meta.row0[b];
   const int br = a.meta.brow[b];           // batch row of q, o and the new token
   const int npages = (T + kPage - 1) / kPage;
-  const int p_begin = split * a.pages_per_split;
+  // sliding window: pages wholly before the first query's window are never read
+  const int p_lo = a.window ? max(0, start - a.window + 1) / kPage : 0;
+  const int p_begin = p_lo + split * a.pages_per_split;
   const int p_end = min(npages, p_begin + a.pages_per_split);
 
   const int wave = threadIdx.x >> 6;
@@ -134,6 +136,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   uint16_t* kpool = static_cast<uint16_t*>(a.k_pool);
   uint16_t* vpool = static_cast<uint16_t*>(a.v_pool);
   const int32_t* trow = a.table + static_cast<int64_t>(seq) * a.table_w;
+  auto tix = [&](int p) { return a.window ? p % a.table_w : p; };   // a windowed cache is a ring
   const int Hkv = a.Hkv;
   const float sl2 = a.scale_log2;
 
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int p_first = p_begin + wave;
   int64_t phys[kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) phys[j] = trow[min(p_first + 4 * j, p_end - 1)];
+  for (int j = 0; j < kBatch; ++j) phys[j] = trow[tix(min(p_first + 4 * j, p_end - 1))];
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + br * a.q_s0 + static_cast<int64_t>(g * G + hl) * a.q_s1 +
                          static_cast<int64_t>(r0 + tl) * a.q_s2;
   u32x4 qw[NQ];
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     // write the new token to the cache: the wave whose page it is, key row by
     // the lanes of row r_new, value column by the lanes of its 4-slot group
     if (p_new >= p_begin && ((p_new - p_begin) & 3) == wave) {
-      const int64_t ph = trow[p_new];
+      const int64_t ph = trow[tix(p_new)];
       if (c16 == r_new) {
         uint16_t* kdst = kpool + ((ph * Hkv + g) * kPage + r_new) * D;
 #pragma unroll
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   for (int p0 = p_first; p0 < p_end; p0 += 4 * kBatch) {
     if (p0 != p_first) {
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) phys[j] = trow[min(p0 + 4 * j, p_end - 1)];
+      for (int j = 0; j < kBatch; ++j) phys[j] = trow[tix(min(p0 + 4 * j, p_end - 1))];
       load_pages(phys, kf, vf);
     }
 #pragma unroll
@@ -295,6 +298,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (key0 + i > qpos) s[i] = -INFINITY;
+      }
+      if (a.window && p * kPage < start + cnt - a.window) {
+        // the page holds keys before the last column's window: per column
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + i <= qpos - a.window) s[i] = -INFINITY;
       }
       if (p * kPage + kPage > T) {
         // stale slots past the length: zero their values so 0 * NaN never occurs

@@ -119,7 +119,7 @@ __device__ __forceinline__ void sload_wait(int& a, int& b) {
 
 }  // namespace
 
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc, int TB) {
   constexpr int NC = D / 16;           // k-steps of the score product
   constexpr int NDB = D / 32;          // 32-row blocks of the output
@@ -185,7 +185,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   // query (loaded once the first key/value tiles are in flight)
   bf16x8 qf[NC];
   const int kv_end = c0 + t0 + qn;            // keys [0, kv_end) can be visible
-  const int ntk = (kv_end + KT - 1) / KT;
+  // sliding window: key tiles wholly before the first query's window are never
+  // read; tile j of this workgroup is key tile kt0 + j
+  const int kt0 = WIN ? max(0, c0 + t0 - a.window + 1) / KT : 0;
+  const int ntk = (kv_end + KT - 1) / KT - kt0;
   const int last_page = (total - 1) >> 4;
   const int32_t* trow = a.table + static_cast<int64_t>(seq) * a.table_w;
   const int Hkv = a.Hkv;
@@ -210,7 +213,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   // wait is placed by the caller (sload_wait), so it never waits on the
   // buffer-to-LDS loads in flight
   auto page_id = [&](int kt) -> int {
-    return sload(trow, static_cast<uint32_t>(min(kt * 4 + wave, last_page)) * 4u);
+    int lp = min((kt0 + kt) * 4 + wave, last_page);
+    if constexpr (WIN) lp = __builtin_amdgcn_readfirstlane(lp % a.table_w);   // a windowed cache is a ring
+    return sload(trow, static_cast<uint32_t>(lp) * 4u);
   };
   auto page_off = [&](int phys) -> uint32_t {
     return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(phys) * Hkv + g) * static_cast<uint32_t>(32 * D);
@@ -288,6 +293,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
       const int lim = qpos - k0 - 8 * half;     // key k0 + 16*(i/8) + 8*half + i%8 visible iff offset <= lim
       if (16 * (i >> 3) + (i & 7) > lim) x0 = -INFINITY;
       if (16 * (i >> 3) + (i & 7) + 1 > lim) x1 = -INFINITY;
+      if constexpr (WIN) {                      // and offset > lim - window
+        if (16 * (i >> 3) + (i & 7) <= lim - a.window) x0 = -INFINITY;
+        if (16 * (i >> 3) + (i & 7) + 1 <= lim - a.window) x1 = -INFINITY;
+      }
     }
     const bf16x2 p = {static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(x0, sl2, mneg))),
                       static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(x1, sl2, mneg)))};
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     const bool has_next = j + 1 < ntk;
     if (has_next) issue_v(pg_v, 1 - P);
     const int nv = page_id(j + 2), nk = page_id(j + 4);
-    const int kbase = j * KT;
+    const int kbase = (kt0 + j) * KT;
     bf16x8 pf[2][2];
     if constexpr (!decltype(any)::value) {
       phase_a(cur, nxt, ks[1 - P], kbase, pf, F_(), T_());
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     }
     // V(j) must have landed; K(j+2) and V(j+1) may still be in flight
     wait_vm((j + 2 < ntk ? NI : 0) + (has_next ? NI : 0));
-    fix_v(j, P);
+    fix_v(kt0 + j, P);
     __syncthreads();
     if (j + 3 < ntk) issue_k(pg_k, 1 - P);
     if constexpr (!decltype(any)::value) phase_b(cur, vs[P], kbase, pf, F_());
@@ -472,25 +481,80 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     qk(ks[0], sA);
-    // reference: maximum of the row's visible keys among keys 0..31
     float mx = -INFINITY;
+    if constexpr (!WIN) {
+      // reference: maximum of the row's visible keys among keys 0..31
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 16 * (i >> 3) + 8 * half + (i & 7);
-      mx = fmaxf(mx, key <= qpos ? sA[0][i] : -INFINITY);
+      for (int i = 0; i < 16; ++i) {
+        const int key = 16 * (i >> 3) + 8 * half + (i & 7);
+        mx = fmaxf(mx, key <= qpos ? sA[0][i] : -INFINITY);
+      }
+    } else {
+      // reference: maximum of the row's visible keys among the first two key
+      // tiles read, which hold every row's first visible key (the rows of a
+      // workgroup start their windows less than 64 keys apart)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt0 * KT + sub * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
+          mx = fmaxf(mx, key <= qpos && key > qpos - a.window ? sA[sub][i] : -INFINITY);
+        }
+      if (ntk > 1) {
+        qk(ks[1], sB);                       // K(1) has landed; step 0 computes these scores again
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = (kt0 + 1) * KT + sub * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
+            mx = fmaxf(mx, key <= qpos && key > qpos - a.window ? sB[sub][i] : -INFINITY);
+          }
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (WIN && mx == -INFINITY) mx = 0.f;    // padding lanes only
     mneg = -(mx * sl2);
     __syncthreads();                         // K(0) is read by every wave before K(2) replaces it
     if (ntk > 2) issue_k(p2, 0);
   }
   // leading tiles wholly visible to the whole workgroup (each with a next
   // tile) in pairs, then the rest with masks
-  const int nfull = min((c0 + t0 + 1) / KT, ntk - 1);
+  const int nfull = min((c0 + t0 + 1) / KT - kt0, ntk - 1);
   int j = 0;
-  for (; j + 2 <= nfull; j += 2) {
-    step(j, sA, sB, F_(), F_());
-    step(j + 1, sB, sA, T_(), F_());
+  if constexpr (WIN) {
+    // one step with the buffers and parity of its index
+    auto one = [&](int jj, auto masked) {
+      if (jj & 1) step(jj, sB, sA, T_(), masked);
+      else step(jj, sA, sB, F_(), masked);
+    };
+    // leading tiles that reach below the last row's window start need masks
+    const int ws_last = max(0, c0 + t0 + qn - a.window);
+    const int jlo = min((ws_last + KT - 1) / KT - kt0, ntk);
+    for (; j + 2 <= jlo; j += 2) {
+      step(j, sA, sB, F_(), T_());
+      step(j + 1, sB, sA, T_(), T_());
+    }
+    if (j < jlo) {
+      step(j, sA, sB, F_(), T_());
+      ++j;
+    }
+    if ((j & 1) && j < nfull) {
+      one(j, F_());
+      ++j;
+    }
+    for (; j + 2 <= nfull; j += 2) {
+      step(j, sA, sB, F_(), F_());
+      step(j + 1, sB, sA, T_(), F_());
+    }
+    if ((j & 1) && j < ntk) {
+      one(j, T_());
+      ++j;
+    }
+  } else {
+    for (; j + 2 <= nfull; j += 2) {
+      step(j, sA, sB, F_(), F_());
+      step(j + 1, sB, sA, T_(), F_());
+    }
   }
   for (; j < ntk; j += 2) {
     step(j, sA, sB, F_(), T_());
@@ -515,8 +579,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kt * KT + sub * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
-          m = fmaxf(m, key <= qpos ? sA[sub][i] : -INFINITY);
+          const int key = (kt0 + kt) * KT + sub * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
+          m = fmaxf(m, key <= qpos && (!WIN || key > qpos - a.window) ? sA[sub][i] : -INFINITY);
         }
       __syncthreads();
     }
@@ -534,12 +598,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
       issue_k(pid, 0);
       issue_v(pid, 0);
       __builtin_amdgcn_s_waitcnt(0);
-      fix_v(kt, 0);
+      fix_v(kt0 + kt, 0);
       __syncthreads();
       qk(ks[0], sA);
       bf16x8 pf[2][2];
-      phase_a(sA, sB, ks[0], kt * KT, pf, T_(), F_());
-      phase_b(sA, vs[0], kt * KT, pf, T_());
+      phase_a(sA, sB, ks[0], (kt0 + kt) * KT, pf, T_(), F_());
+      phase_b(sA, vs[0], (kt0 + kt) * KT, pf, T_());
       __syncthreads();
     }
     l = l0 + l1;
@@ -582,10 +646,16 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   const int Tq = 32 * ps.TB;
   dim3 grid(a.Hkv * (G / ps.Gc), a.nseq, (a.n_rect + Tq - 1) / Tq);
   dim3 block(256);
-  if (a.d == 128)
-    hipLaunchKernelGGL((prefill_bf16_kernel<128>), grid, block, 0, s, a, ps.Gc, ps.TB);
-  else
-    hipLaunchKernelGGL((prefill_bf16_kernel<64>), grid, block, 0, s, a, ps.Gc, ps.TB);
+  if (a.window) {
+    if (a.d == 128)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a, ps.Gc, ps.TB);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a, ps.Gc, ps.TB);
+  } else if (a.d == 128) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a, ps.Gc, ps.TB);
+  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a, ps.Gc, ps.TB);
+  }
   return hipGetLastError();
 }
 

@@ -89,7 +89,23 @@ typedef struct gqa_tensor {
  *                    library's convention).  Keys are cached AFTER rotation
  *                    ([P1] 2.5: the cache holds the keys used by attention).
  *  max_position      rotation table rows: positions 0..max_position-1.
- *  rope_theta        rotation base: pair i turns by p * theta^(-2i/d).      */
+ *  rope_theta        rotation base: pair i turns by p * theta^(-2i/d).
+ *  window            sliding window W ([P3] sliding-window lesson: a query at
+ *                    position t reads positions t-W+1..t, itself included);
+ *                    0 = full causal attention.  W > 0 makes the cache a ring:
+ *                    a sequence's block table holds at most max_pages_per_seq
+ *                    entries and logical page L lives in entry L mod
+ *                    max_pages_per_seq, so once the ring is full each new
+ *                    logical page overwrites, in place, the page of the one
+ *                    max_pages_per_seq before it.  max_pages_per_seq must be at
+ *                    least ceil(W/16) + 1 (GQA_ERR_UNSUPPORTED).  A call that
+ *                    writes positions [c, c+n) needs [max(0, c-W+1), c+n) to
+ *                    fit in max_pages_per_seq consecutive logical pages
+ *                    (GQA_ERR_OUT_OF_PAGES: split a long prompt into chunks).
+ *                    Ring sequences are truncated only to 0 or to at least
+ *                    their length, and are not forked (GQA_ERR_UNSUPPORTED);
+ *                    gqa_attention queries must have their whole window still
+ *                    in the ring (GQA_ERR_POSITION).                        */
 typedef struct gqa_cache_config {
   int32_t num_layers;
   int32_t num_kv_heads;
@@ -102,6 +118,7 @@ typedef struct gqa_cache_config {
   int32_t rope_style;
   int32_t max_position;
   double rope_theta;
+  int32_t window;
 } gqa_cache_config;
 
 typedef struct gqa_cache gqa_cache;

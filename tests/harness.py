@@ -27,17 +27,17 @@ class Pair:
     """One library cache and one oracle cache with the same configuration."""
 
     def __init__(self, num_layers, Hkv, d, num_pages, max_seqs, max_pages_per_seq, dtype,
-                 theta, max_position=None, free_order=None):
+                 theta, max_position=None, free_order=None, window=0):
         import causal_gqa_attention_attn_amd as lib
         self.lib = lib
         self.dtype = dtype
         mp = max_position if max_position else max_pages_per_seq * 16
         self.gpu = lib.PagedCache(num_layers, Hkv, d, num_pages, max_seqs, max_pages_per_seq,
                                   dtype=dtype, rope_theta=theta, max_position=mp,
-                                  free_list_order=free_order)
+                                  free_list_order=free_order, window=window)
         self.ref = CacheModel(num_layers, Hkv, d, 16, num_pages, max_seqs, max_pages_per_seq,
                               dtype=dtype_tag(dtype), rope_theta=theta, max_position=mp,
-                              free_order=free_order)
+                              free_order=free_order, window=window)
         self.ws = None
 
     def workspace(self, B, Hq):
@@ -131,8 +131,9 @@ class Pair:
                 assert self.gpu.device_table(s, len(host_table)) == host_table, f"device table of sequence {s}"
             for l in (layers if layers is not None else range(self.ref.L)):
                 assert self.lib.gqa_cache_length(self.gpu.handle, s, l) == self.ref.cache_length(s, l)
-                k, v = self.gpu.gather(s, l)
-                rk, rv = self.ref.keys(s, l), self.ref.values(s, l)
+                first, k, v = self.gpu.gather_resident(s, l)
+                assert first == self.ref.resident_from(s, l)
+                rk, rv = self.ref.keys(s, l)[:, first:], self.ref.values(s, l)[:, first:]
                 assert k.shape == rk.shape, (k.shape, rk.shape)
                 kk = k.to(torch.float32).numpy()
                 vv = v.to(torch.float32).numpy()
