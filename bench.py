@@ -33,6 +33,9 @@ truncates between calls), median and minimum of 5 such batches:
     8192-token prompt with 512 tokens of their own (prefix sharing);
   * masks with holes: the Llama-shaped prefill with 1536 valid tokens per
     row in 16 runs separated by padding, beside the same tokens right-padded;
+  * sliding window of 4096 positions: the Grok-shaped prefill (flops
+    4*Hq*d per visible (query, key) pair) and gqa_decode of the 64 serving
+    sequences over ring caches (K/V bytes of the window);
   * edit re-prefill: 16 sequences of 4096 tokens, each truncated at a seeded
     m_b and its suffix re-prefilled (gqa_prefill on a non-empty cache);
     flops 2*Hq*d*(n^2 - m_b^2).
@@ -248,9 +251,9 @@ def other_configs(lib, W):
         # the padding rows: a random leading gap, 15 inner gaps of at least one row, a tail
         extra = rng.multinomial(sh.n - nv - (runs - 1), [1.0 / (runs + 1)] * (runs + 1))
         rows, r = [], int(extra[0])
-        for k in range(runs):
+        for run in range(runs):
             rows.extend(range(r, r + per_run))
-            r += per_run + (1 + int(extra[k + 1]) if k + 1 < runs else 0)
+            r += per_run + (1 + int(extra[run + 1]) if run + 1 < runs else 0)
         hole_rows.append(rows)
     inp = W.prefill_inputs(W.AttnShape(B=sh.B, n=sh.n, Hq=sh.Hq, Hkv=sh.Hkv, d=sh.d, dtype=sh.dtype,
                                        theta=sh.theta), 1008, lengths=[nv] * sh.B)
@@ -276,6 +279,53 @@ def other_configs(lib, W):
         "right_padded_ms_median": round(rmed, 4)}
     pre.close()
     del Qh, Kh, Vh, Oh
+    # sliding window W = 4096: the Grok-shaped prefill (one call, the ring holds the
+    # whole prompt) and one decode step of the 64 serving sequences (rings of
+    # 4096 + 2048 tokens, filled in 2048-token chunks)
+    WIN = 4096
+    sh = W.GROK
+    inp = W.grok()
+    Qg, Kg, Vg = inp.Q.cuda(), inp.K.cuda(), inp.V.cuda()
+    Og = torch.empty_like(Qg)
+    wc = lib.PagedCache(1, sh.Hkv, sh.d, sh.n // 16 + 8, 1, sh.n // 16 + 2, dtype=torch.bfloat16,
+                        rope_theta=sh.theta, max_position=sh.n + 32, window=WIN)
+    med, mn = _median_ms(lambda: lib.gqa_prefill(wc.handle, 0, [0], Qg, Kg, Vg, inp.mask, inp.positions, Og),
+                         before=lambda: lib.kv_cache_truncate(wc.handle, 0, 0), iters=10, reps=3)
+    visible = sum(min(p + 1, WIN) for p in range(sh.n))
+    flops = 4.0 * sh.Hq * sh.d * visible
+    res["window_prefill"] = {
+        "workload": "gqa_prefill B=1 n=8192 Hq=48 Hkv=8 d=128 with a 4096-position sliding window",
+        "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+        "frac": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "ms_median": round(med, 4), "ms_min": round(mn, 4)}
+    wc.close()
+    del Qg, Kg, Vg, Og
+    sh = W.SERVING
+    R = WIN // 16 + 1 + 2048 // 16
+    lens = W.serving_lengths()
+    pages = sum(min(R, -(-(x + 1) // 16)) for x in lens) + 8
+    wc = lib.PagedCache(1, sh.Hkv, sh.d, pages, Bs, R, dtype=torch.bfloat16, rope_theta=sh.theta,
+                        max_position=32770, free_list_order=W.page_order(pages, 1009), window=WIN)
+    for b, L in enumerate(lens):
+        for c0 in range(0, L, 2048):
+            n = min(2048, L - c0)
+            kf = W.normal_device((1, sh.Hkv, n, sh.d), 94000 + b * 16 + c0 // 2048)
+            vf = W.normal_device((1, sh.Hkv, n, sh.d), 95000 + b * 16 + c0 // 2048)
+            lib.kv_cache_append(wc.handle, 0, [b], kf, vf, torch.ones((1, n), dtype=torch.uint8),
+                                torch.arange(c0, c0 + n, dtype=torch.int32)[None])
+    del kf, vf
+    ids = list(range(Bs))
+    wws = torch.zeros(lib.gqa_workspace_size(wc.handle, Bs, sh.Hq), dtype=torch.uint8, device="cuda")
+    # gqa_decode (the attention read alone): a ring is not truncated back between calls
+    med, mn = _median_ms(lambda: lib.gqa_decode(wc.handle, 0, ids, q, lens, o, wws))
+    nbytes = sum(min(L, WIN) * 2 * sh.Hkv * sh.d * 2 for L in lens)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    res["window_decode"] = {
+        "workload": "gqa_decode of the 64 serving sequences with a 4096-position sliding window over "
+                    "ring caches, Hq=32 Hkv=8 d=128, one layer",
+        "kv_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+        "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1)}
+    wc.close()
     # edit re-prefill
     sh = W.EDIT
     full = W.prefill_inputs(sh, 1006)
