@@ -486,8 +486,8 @@ def main():
                    "causal_flops": flops, "causal_flops_exact": 2.0 * HQ * D * N * (N + 1)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic("prefill_bf16_kernel<128>", src_prefill),
-                     "kernel": "prefill_bf16_kernel<128>"},
+                     "traffic": _traffic("prefill_bf16_kernel<128, false>", src_prefill),
+                     "kernel": "prefill_bf16_kernel<128, false>"},
     }
     if not args.prefill_only:
         span_ms = mean([e[3].elapsed_time(e[4]) for e in events])
