@@ -500,8 +500,8 @@ def main():
         src_dec = os.path.join(ROOT, "causal_gqa_attention_attn_amd", "csrc", "decode_bf16.hip")
         out["roofline_decode"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                                   "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                                  "traffic": _traffic("decode_bf16_kernel<128>", src_dec),
-                                  "kernel": "one layer of the replayed decode graph: decode_bf16_kernel<128> "
+                                  "traffic": _traffic("decode_bf16_kernel<128, false, false>", src_dec),
+                                  "kernel": "one layer of the replayed decode graph: decode_bf16_kernel<128, false, false> "
                                             "(append, split-T attention and split combine), 32 MiB of K/V",
                                   "layer_us": round(per_layer_ms * 1e3, 2)}
     if not args.no_other_configs and not args.prefill_only:

@@ -57,7 +57,10 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 
 }  // namespace
 
-template <int D>
+// CHUNK: some sequence brings more than one query (or rectangular padding
+// rows); WIN: the cache has a sliding window.  Plain decode takes neither, so
+// its instructions carry no per-column position arithmetic.
+template <int D, bool CHUNK, bool WIN>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NQ = D / 32;      // k-steps of the score product
   constexpr int NDB = D / 16;     // 16-row blocks of the output
@@ -69,15 +72,24 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int G = a.Hq / a.Hkv;
   const int hchunks = (a.ncol + 15) >> 4;
   const int gy = a.Hkv * hchunks;          // (kv head, column chunk) rows of the split records
-  // blockIdx.x = (split, column chunk, kv head), kv head fastest: the
+  // Chunks: blockIdx.x = (split, column chunk, kv head), kv head fastest: the
   // workgroups running at one time cover every kv head of the same few pages
   // (whole 32 KiB page rows of the pool), and the column chunks of one (split,
   // kv head) run Hkv workgroups apart, on the same XCD (workgroup index mod 8)
   // when Hkv is a multiple of 8, so the later chunks find the pages in its L2.
-  const int g = blockIdx.x % a.Hkv;
-  const int xr = blockIdx.x / a.Hkv;
-  const int hcb = xr % hchunks;
-  const int gsplit = xr / hchunks;
+  // Plain decode: blockIdx.x = split, blockIdx.y = (kv head, column chunk),
+  // which measured faster for a single long sequence.
+  int g, hcb, gsplit;
+  if constexpr (CHUNK) {
+    g = blockIdx.x % a.Hkv;
+    const int xr = blockIdx.x / a.Hkv;
+    hcb = xr % hchunks;
+    gsplit = xr / hchunks;
+  } else {
+    g = blockIdx.y / hchunks;
+    hcb = blockIdx.y - g * hchunks;
+    gsplit = blockIdx.x;
+  }
   const int yrow = g * hchunks + hcb;
   int b = 0;
   while (b + 1 < a.nseq && a.split_off[b + 1] <= gsplit) ++b;
@@ -86,12 +98,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int seq = a.meta.seq[b];
   const int T = a.meta.total[b];
   const int start = a.meta.start[b];
-  const int cnt = a.meta.count[b];
-  const int r0 = a.meta.row0[b];
+  const int cnt = CHUNK ? a.meta.count[b] : 1;
+  const int r0 = CHUNK ? a.meta.row0[b] : 0;
   const int br = a.meta.brow[b];           // batch row of q, o and the new token
   const int npages = (T + kPage - 1) / kPage;
   // sliding window: pages wholly before the first query's window are never read
-  const int p_lo = a.window ? max(0, start - a.window + 1) / kPage : 0;
+  const int p_lo = WIN ? max(0, start - a.window + 1) / kPage : 0;
   const int p_begin = p_lo + split * a.pages_per_split;
   const int p_end = min(npages, p_begin + a.pages_per_split);
 
@@ -102,7 +114,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 
   // padding rows of o (rectangular rows outside the sequence's query run) -> 0,
   // by the first split of the first column chunk of each kv head
-  if (split == 0 && hcb == 0 && a.n_rect > cnt) {
+  if (CHUNK && split == 0 && hcb == 0 && a.n_rect > cnt) {
     for (int idx = threadIdx.x; idx < G * a.n_rect * (D / 8); idx += 256) {
       const int hh = idx / (a.n_rect * (D / 8));
       const int rem = idx - hh * a.n_rect * (D / 8);
@@ -122,13 +134,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int cl = hcb * 16 + c16;                // this lane's column
   const bool hvalid = cl < cnt * G;
   const int clc = min(cl, cnt * G - 1);
-  const int tl = clc / G;                       // its query token and head
+  const int tl = CHUNK ? clc / G : 0;           // its query token and head
   const int hl = clc - tl * G;
   const int qpos = start + tl;                  // the query's position: keys 0..qpos are visible
   // o row of column c of this chunk
   auto out_row = [&](int c) {
     const int col = hcb * 16 + c;
-    const int t = col / G;
+    const int t = CHUNK ? col / G : 0;
     return static_cast<uint16_t*>(a.o) + br * a.o_s0 + static_cast<int64_t>(g * G + col - t * G) * a.o_s1 +
            static_cast<int64_t>(r0 + t) * a.o_s2;
   };
@@ -136,7 +148,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   uint16_t* kpool = static_cast<uint16_t*>(a.k_pool);
   uint16_t* vpool = static_cast<uint16_t*>(a.v_pool);
   const int32_t* trow = a.table + static_cast<int64_t>(seq) * a.table_w;
-  auto tix = [&](int p) { return a.window ? p % a.table_w : p; };   // a windowed cache is a ring
+  auto tix = [&](int p) { return WIN ? p % a.table_w : p; };   // a windowed cache is a ring
   const int Hkv = a.Hkv;
   const float sl2 = a.scale_log2;
 
@@ -299,7 +311,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i)
           if (key0 + i > qpos) s[i] = -INFINITY;
       }
-      if (a.window && p * kPage < start + cnt - a.window) {
+      if (WIN && p * kPage < start + cnt - a.window) {
         // the page holds keys before the last column's window: per column
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -499,11 +511,25 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s) {
   const int hchunks = (a.ncol + 15) / 16;
-  dim3 grid(total_splits * hchunks * a.Hkv);
-  if (a.d == 128)
-    hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(256), 0, s, a);
+  bool chunk = a.ncol != a.Hq / a.Hkv || a.n_rect != 1;
+  for (int j = 0; j < a.nseq && !chunk; ++j) chunk = a.meta.count[j] != 1 || a.meta.row0[j] != 0;
+  const dim3 grid = chunk ? dim3(total_splits * hchunks * a.Hkv) : dim3(total_splits, a.Hkv * hchunks);
+  const bool win = a.window != 0;
+  auto pick = [&](auto dv, auto cv, auto wv) {
+    hipLaunchKernelGGL((decode_bf16_kernel<decltype(dv)::value, decltype(cv)::value, decltype(wv)::value>), grid,
+                       dim3(256), 0, s, a);
+  };
+  using D128 = std::integral_constant<int, 128>;
+  using D64 = std::integral_constant<int, 64>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (a.d == 128) {
+    if (chunk) win ? pick(D128(), T_(), T_()) : pick(D128(), T_(), F_());
+    else win ? pick(D128(), F_(), T_()) : pick(D128(), F_(), F_());
+  } else {
+    if (chunk) win ? pick(D64(), T_(), T_()) : pick(D64(), T_(), F_());
+    else win ? pick(D64(), F_(), T_()) : pick(D64(), F_(), F_());
+  }
   return hipGetLastError();
 }
 
