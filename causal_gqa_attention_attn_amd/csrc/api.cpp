@@ -660,7 +660,7 @@ GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, cons
     const int32_t have = c->len[static_cast<int64_t>(seq_ids[b]) * cf.num_layers + layer];
     if (count[b] && (start[b] < 0 || static_cast<int64_t>(start[b]) + count[b] > have))
       return fail(GQA_ERR_POSITION, "query positions must lie inside the cached length");
-    if (count[b] && start[b] - cf.window + 1 < resident_from(cf, have))
+    if (count[b] && std::max(0, start[b] - cf.window + 1) < resident_from(cf, have))
       return fail(GQA_ERR_POSITION, "the window of a query reaches positions the ring no longer holds");
     totals[b] = have;
   }

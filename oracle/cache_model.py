@@ -311,7 +311,7 @@ class CacheModel:
         Used to check sampled outputs of large runs without recomputing all rows.
         """
         pos = np.asarray(positions, dtype=np.int64)
-        if self.window and pos.size and pos.min() - self.window + 1 < self.resident_from(seq, layer):
+        if self.window and pos.size and max(0, pos.min() - self.window + 1) < self.resident_from(seq, layer):
             raise OracleError("POSITION", "the window of a query reaches positions the ring no longer holds")
         q_used = round_to_storage(rotate(np.asarray(q_rows, np.float32), pos, self.theta), self.dtype)
         key = (seq, layer)

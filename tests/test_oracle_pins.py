@@ -474,6 +474,9 @@ def check_ring_cache():
         m.prefill_rows(0, 0, np.zeros((1, 1, 4), np.float32), [30])
     assert e.value.code == "POSITION"
     m.prefill_rows(0, 0, np.zeros((1, 1, 4), np.float32), [35])
+    short = _model(num_pages=8, max_pages_per_seq=3, window=20, max_position=256)
+    _append(short, 0, [0], [10], [0], rng)
+    short.prefill_rows(0, 0, np.zeros((1, 1, 4), np.float32), [5])   # window starts before 0: nothing lost
     m.truncate(0, 0)
     assert m.page_table(0) == [] and list(m.free)[-3:] == [0, 1, 2] and m.check() == []
     with pytest.raises(OracleError) as e:
