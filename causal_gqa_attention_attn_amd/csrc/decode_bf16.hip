@@ -59,38 +59,42 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 
 // CHUNK: some sequence brings more than one query (or rectangular padding
 // rows); WIN: the cache has a sliding window.  Plain decode takes neither, so
-// its instructions carry no per-column position arithmetic.
+// its instructions carry no per-column position arithmetic.  In chunk mode a
+// workgroup takes two 16-column chunks of its kv head, which share every K/V
+// load.
 template <int D, bool CHUNK, bool WIN>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NQ = D / 32;      // k-steps of the score product
   constexpr int NDB = D / 16;     // 16-row blocks of the output
-  __shared__ float red_m[4][16];
-  __shared__ float red_l[4][16];
-  __shared__ float red_o[4][16][D + 4];
+  constexpr int NCH = CHUNK ? 2 : 1;   // 16-column chunks per workgroup
+  __shared__ float red_m[4][16 * NCH];
+  __shared__ float red_l[4][16 * NCH];
+  __shared__ float red_o[4][16 * NCH][D + 4];
   __shared__ int s_ok;
 
   const int G = a.Hq / a.Hkv;
-  const int hchunks = (a.ncol + 15) >> 4;
-  const int gy = a.Hkv * hchunks;          // (kv head, column chunk) rows of the split records
-  // Chunks: blockIdx.x = (split, column chunk, kv head), kv head fastest: the
+  const int hchunks = (a.ncol + 15) >> 4;           // 16-column chunks per kv head
+  const int hgroups = (hchunks + NCH - 1) / NCH;    // workgroup rows per kv head
+  const int gy = a.Hkv * hchunks;                   // (kv head, column chunk) rows of the split records
+  // Chunks: blockIdx.x = (split, chunk group, kv head), kv head fastest: the
   // workgroups running at one time cover every kv head of the same few pages
-  // (whole 32 KiB page rows of the pool), and the column chunks of one (split,
+  // (whole 32 KiB page rows of the pool), and the chunk groups of one (split,
   // kv head) run Hkv workgroups apart, on the same XCD (workgroup index mod 8)
-  // when Hkv is a multiple of 8, so the later chunks find the pages in its L2.
+  // when Hkv is a multiple of 8, so the later ones find the pages in its L2.
   // Plain decode: blockIdx.x = split, blockIdx.y = (kv head, column chunk),
   // which measured faster for a single long sequence.
-  int g, hcb, gsplit;
+  int g, hgr, gsplit;
   if constexpr (CHUNK) {
     g = blockIdx.x % a.Hkv;
     const int xr = blockIdx.x / a.Hkv;
-    hcb = xr % hchunks;
-    gsplit = xr / hchunks;
+    hgr = xr % hgroups;
+    gsplit = xr / hgroups;
   } else {
     g = blockIdx.y / hchunks;
-    hcb = blockIdx.y - g * hchunks;
+    hgr = blockIdx.y - g * hchunks;
     gsplit = blockIdx.x;
   }
-  const int yrow = g * hchunks + hcb;
+  const int hcb0 = hgr * NCH;                       // first column chunk of this workgroup
   int b = 0;
   while (b + 1 < a.nseq && a.split_off[b + 1] <= gsplit) ++b;
   const int split = gsplit - a.split_off[b];
@@ -113,8 +117,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int c16 = lane & 15;
 
   // padding rows of o (rectangular rows outside the sequence's query run) -> 0,
-  // by the first split of the first column chunk of each kv head
-  if (CHUNK && split == 0 && hcb == 0 && a.n_rect > cnt) {
+  // by the first split of the first chunk group of each kv head
+  if (CHUNK && split == 0 && hgr == 0 && a.n_rect > cnt) {
     for (int idx = threadIdx.x; idx < G * a.n_rect * (D / 8); idx += 256) {
       const int hh = idx / (a.n_rect * (D / 8));
       const int rem = idx - hh * a.n_rect * (D / 8);
@@ -128,18 +132,26 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     }
   }
   // Columns of the matrix products are (query token t, head h) pairs, column
-  // c = t*G + h; this workgroup holds columns 16*hcb .. 16*hcb + 15.
-  const int Gc = min(16, cnt * G - hcb * 16);   // valid columns of this chunk for this sequence
-  if (Gc <= 0) return;                          // (every split of the chunk returns here)
-  const int cl = hcb * 16 + c16;                // this lane's column
-  const bool hvalid = cl < cnt * G;
-  const int clc = min(cl, cnt * G - 1);
-  const int tl = CHUNK ? clc / G : 0;           // its query token and head
-  const int hl = clc - tl * G;
-  const int qpos = start + tl;                  // the query's position: keys 0..qpos are visible
-  // o row of column c of this chunk
-  auto out_row = [&](int c) {
-    const int col = hcb * 16 + c;
+  // c = t*G + h; chunk ch of this workgroup holds columns 16*(hcb0+ch) + 0..15.
+  int Gc[NCH];                                  // valid columns of each chunk for this sequence
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) Gc[ch] = min(16, cnt * G - (hcb0 + ch) * 16);
+  if (Gc[0] <= 0) return;                       // (every split of the group returns here)
+  const bool two = NCH > 1 && Gc[NCH - 1] > 0;  // the second chunk has columns
+  bool hvalid[NCH];
+  int hl[NCH], tl[NCH], qpos[NCH];              // this lane's column: head, token, position
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int cl = (hcb0 + ch) * 16 + c16;
+    hvalid[ch] = cl < cnt * G;
+    const int clc = min(cl, cnt * G - 1);
+    tl[ch] = CHUNK ? clc / G : 0;
+    hl[ch] = clc - tl[ch] * G;
+    qpos[ch] = start + tl[ch];                  // keys 0..qpos are visible
+  }
+  // o row of column c of chunk ch
+  auto out_row = [&](int ch, int c) {
+    const int col = (hcb0 + ch) * 16 + c;
     const int t = CHUNK ? col / G : 0;
     return static_cast<uint16_t*>(a.o) + br * a.o_s0 + static_cast<int64_t>(g * G + col - t * G) * a.o_s1 +
            static_cast<int64_t>(r0 + t) * a.o_s2;
@@ -153,24 +165,27 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const float sl2 = a.scale_log2;
 
   // the step's new token (slot T-1) lives in the last page, so in the last split
-  const bool owns_new = a.k_new != nullptr && split == nsplit - 1;
+  const bool owns_new = !CHUNK && a.k_new != nullptr && split == nsplit - 1;
   const int p_new = (T - 1) >> 4;
   const int r_new = (T - 1) & 15;
 
   // Everything the first batch needs is requested before anything is used:
-  // the block-table entries of this wave's pages, the query, its rotation row
-  // and the new token.  Loads are unconditional (indices clamped to valid
+  // the block-table entries of this wave's pages, the queries, their rotation
+  // rows and the new token.  Loads are unconditional (indices clamped to valid
   // rows) so the compiler issues them back to back.
   constexpr int kBatch = GQA_DECODE_BATCH;
   const int p_first = p_begin + wave;
   int64_t phys[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) phys[j] = trow[tix(min(p_first + 4 * j, p_end - 1))];
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + br * a.q_s0 + static_cast<int64_t>(g * G + hl) * a.q_s1 +
-                         static_cast<int64_t>(r0 + tl) * a.q_s2;
-  u32x4 qw[NQ];
+  u32x4 qw[NCH][NQ];
 #pragma unroll
-  for (int c = 0; c < NQ; ++c) qw[c] = *reinterpret_cast<const u32x4*>(qrow + c * 32 + grp * 8);
+  for (int ch = 0; ch < NCH; ++ch) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + br * a.q_s0 +
+                           static_cast<int64_t>(g * G + hl[ch]) * a.q_s1 + static_cast<int64_t>(r0 + tl[ch]) * a.q_s2;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) qw[ch][c] = *reinterpret_cast<const u32x4*>(qrow + c * 32 + grp * 8);
+  }
   u32x4 kw[NQ];
   uint32_t vw[NDB];
   if (owns_new) {
@@ -181,19 +196,22 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vw[db] = vrow[db * 16 + c16];
   }
-  float cs[NQ / 2][8][2];
+  float cs[NCH][NQ / 2][8][2];
   if (a.rope) {
-    const float* rrow = a.rope + static_cast<int64_t>(qpos) * D;
 #pragma unroll
-    for (int c = 0; c < NQ / 2; ++c) {
-      const float4* r4 = reinterpret_cast<const float4*>(rrow + 2 * (c * 32 + grp * 8));
+    for (int ch = 0; ch < NCH; ++ch) {
+      const float* rrow = a.rope + static_cast<int64_t>(qpos[ch]) * D;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float4 v = r4[e];
-        cs[c][2 * e][0] = v.x;
-        cs[c][2 * e][1] = v.y;
-        cs[c][2 * e + 1][0] = v.z;
-        cs[c][2 * e + 1][1] = v.w;
+      for (int c = 0; c < NQ / 2; ++c) {
+        const float4* r4 = reinterpret_cast<const float4*>(rrow + 2 * (c * 32 + grp * 8));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 v = r4[e];
+          cs[ch][c][2 * e][0] = v.x;
+          cs[ch][c][2 * e][1] = v.y;
+          cs[ch][c][2 * e + 1][0] = v.z;
+          cs[ch][c][2 * e + 1][1] = v.w;
+        }
       }
     }
   }
@@ -214,9 +232,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   u32x2 vf[kBatch][NDB];
   load_pages(phys, kf, vf);
 
-  // rotate (pairs i, i + D/2) and round to bf16: the query, and the new key
-  // with the same rotation row
-  auto rotate_round = [&](const u32x4* w_in, bool valid, bf16x8* out) {
+  // rotate (pairs i, i + D/2) with rotation row csr and round to bf16: the
+  // queries, and the new key with the query's rotation row
+  auto rotate_round = [&](const u32x4* w_in, bool valid, const float (&csr)[NQ / 2][8][2], bf16x8* out) {
     float x[NQ][8];
 #pragma unroll
     for (int c = 0; c < NQ; ++c)
@@ -232,7 +250,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float lo, hi;
-          rotate_pair(x[c][e], x[c + NQ / 2][e], cs[c][e][0], cs[c][e][1], lo, hi);
+          rotate_pair(x[c][e], x[c + NQ / 2][e], csr[c][e][0], csr[c][e][1], lo, hi);
           x[c][e] = lo;
           x[c + NQ / 2][e] = hi;
         }
@@ -245,11 +263,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
       out[c] = __builtin_bit_cast(bf16x8, w);
     }
   };
-  bf16x8 qf[NQ];
-  rotate_round(qw, hvalid, qf);
+  bf16x8 qf[NCH][NQ];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) rotate_round(qw[ch], hvalid[ch], cs[ch], qf[ch]);
   bf16x8 knew[NQ];
   if (owns_new) {
-    rotate_round(kw, true, knew);
+    rotate_round(kw, true, cs[0], knew);
     // write the new token to the cache: the wave whose page it is, key row by
     // the lanes of row r_new, value column by the lanes of its 4-slot group
     if (p_new >= p_begin && ((p_new - p_begin) & 3) == wave) {
@@ -267,11 +286,15 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     }
   }
 
-  f32x4 o[NDB];
+  f32x4 o[NCH][NDB];
+  float m_run[NCH], l_run[NCH];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -1e30f;
-  float l_run = 0.f;
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[ch][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[ch] = -1e30f;
+    l_run[ch] = 0.f;
+  }
 
   // wave w takes pages p_begin + w, + 4, ...; kBatch of them are in flight at
   // a time (pages past the split's end reload its last page and are skipped)
@@ -300,23 +323,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
           }
         }
       }
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][c], qf[c], s, 0, 0, 0);
       const int key0 = p * kPage + grp * 4;   // keys of this lane's rows: key0 + i
-      if (p * kPage + kPage > start + 1) {
-        // the page holds keys past the first query's position: causal mask
-        // per column (covers the keys at or past T, since every qpos < T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (key0 + i > qpos) s[i] = -INFINITY;
-      }
-      if (WIN && p * kPage < start + cnt - a.window) {
-        // the page holds keys before the last column's window: per column
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (key0 + i <= qpos - a.window) s[i] = -INFINITY;
-      }
       if (p * kPage + kPage > T) {
         // stale slots past the length: zero their values so 0 * NaN never occurs
         const uint32_t k01 = (key0 < T ? 0x0000ffffu : 0u) | (key0 + 1 < T ? 0xffff0000u : 0u);
@@ -327,193 +334,227 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
           vf[j][db][1] &= k23;
         }
       }
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -m_new));
-      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      s16x4 pb;
+      for (int ch = 0; ch < NCH; ++ch) {
+        if (ch > 0 && !two) break;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(short, static_cast<__bf16>(pr[i]));
+        for (int c = 0; c < NQ; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][c], qf[ch][c], s, 0, 0, 0);
+        if (p * kPage + kPage > start + 1) {
+          // the page holds keys past the first query's position: causal mask
+          // per column (covers the keys at or past T, since every qpos < T)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        o[db] *= alpha;
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf[j][db]), pb, o[db], 0, 0,
-                                                          0);
+          for (int i = 0; i < 4; ++i)
+            if (key0 + i > qpos[ch]) s[i] = -INFINITY;
+        }
+        if (WIN && p * kPage < start + cnt - a.window) {
+          // the page holds keys before the last column's window: per column
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + i <= qpos[ch] - a.window) s[i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[ch], mx * sl2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[ch] - m_new);
+        m_run[ch] = m_new;
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -m_new));
+        l_run[ch] = l_run[ch] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        s16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(short, static_cast<__bf16>(pr[i]));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          o[ch][db] *= alpha;
+          o[ch][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf[j][db]), pb,
+                                                                o[ch][db], 0, 0, 0);
+        }
       }
     }
   }
 
-  // combine the four waves: lane (head c16, grp) holds o rows d = 16*db + 4*grp + i
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (grp == 0) {
-    red_m[wave][c16] = m_run;
-    red_l[wave][c16] = l_tot;
+  // combine the four waves: lane (column c16, grp) holds o rows d = 16*db + 4*grp + i
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    float l_tot = l_run[ch] + __shfl_xor(l_run[ch], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (grp == 0) {
+      red_m[wave][ch * 16 + c16] = m_run[ch];
+      red_l[wave][ch * 16 + c16] = l_tot;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red_o[wave][ch * 16 + c16][db * 16 + grp * 4 + i] = o[ch][db][i];
   }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red_o[wave][c16][db * 16 + grp * 4 + i] = o[db][i];
   __syncthreads();
 
-  // 256 threads: head column hh = tid / 16; thread dl holds d = E*dl .. E*dl + E-1
+  // 256 threads: column hh = tid / 16 of a chunk; thread dl holds d = E*dl .. E*dl + E-1
   constexpr int E = D / 16;
   const int hh = threadIdx.x >> 4;
   const int dl = threadIdx.x & 15;
-  const bool hv2 = hh < Gc;
-  float M = red_m[0][hh];
+  for (int ch = 0; ch < NCH; ++ch) {
+    if (Gc[ch] <= 0) break;
+    const int col = ch * 16 + hh;
+    const bool hv2 = hh < Gc[ch];
+    float M = red_m[0][col];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
-  float L = 0.f;
-  float acc[E];
-  {
-    float sc[4];
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][col]);
+    float L = 0.f;
+    float acc[E];
+    {
+      float sc[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      sc[w] = __builtin_amdgcn_exp2f(red_m[w][hh] - M);
-      L += red_l[w][hh] * sc[w];
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) v += red_o[w][hh][E * dl + e] * sc[w];
-      acc[e] = v;
-    }
-  }
-  if (nsplit == 1) {
-    if (!hv2) return;
-    const float inv = 1.f / L;
-    uint16_t* orow = out_row(hh);
-    uint32_t w[E / 2];
-#pragma unroll
-    for (int e = 0; e < E / 2; ++e) w[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    if constexpr (E == 8)
-      *reinterpret_cast<u32x4*>(orow + E * dl) = u32x4{w[0], w[1], w[2], w[3]};
-    else
-      *reinterpret_cast<u32x2*>(orow + E * dl) = u32x2{w[0], w[1]};
-    return;
-  }
-
-  // Split records of this (sequence, kv head, column chunk): o rows [split][column in chunk][D]
-  // and (m, l) headers [split][head in chunk], written and read with
-  // device-scope (sc1) buffer accesses, which stay coherent across the XCDs'
-  // L2 caches.  The last K splits are also mergers: merger j combines output
-  // columns [j*D/K, (j+1)*D/K) of every head.  Flags: one row of nsplit per
-  // merger, so a merger clears its own row without racing another's wait.
-  const int K = nsplit >= kDecodeMergers ? kDecodeMergers : 2;   // divides D/4
-  const int mj = split - (nsplit - K);          // merger index, negative for the others
-  const int64_t group = static_cast<int64_t>(a.split_off[b]) * gy + static_cast<int64_t>(yrow) * nsplit;
-  int32_t* flags = a.flags + group * kDecodeMergers;
-  const __amdgpu_buffer_rsrc_t ro =
-      __builtin_amdgcn_make_buffer_rsrc(a.part_o + group * (16 * D), 0, nsplit * Gc * D * 4, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rh =
-      __builtin_amdgcn_make_buffer_rsrc(a.part_h + group * (16 * 2), 0, nsplit * Gc * 2 * 4, kBufferWord3);
-  if (hv2) {
-    const int rec = split * Gc + hh;
-#pragma unroll
-    for (int e = 0; e < E; e += 4)
-      __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(u32x4, f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]}), ro,
-          (rec * D + E * dl + e) * 4, 0, kSc1);
-    if (dl == 0) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, float2_t{M, L}), rh, rec * 8, 0, kSc1);
-  }
-  __builtin_amdgcn_s_waitcnt(0);        // this thread's record has reached the device
-  __syncthreads();
-  if (static_cast<int>(threadIdx.x) < K && static_cast<int>(threadIdx.x) != mj)
-    __hip_atomic_store(flags + threadIdx.x * nsplit + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (mj < 0) return;
-
-  // Merger: wait (bounded) for every other split's record.  Then each of this
-  // merger's (head, column) pairs is spread over F adjacent lanes (F a power
-  // of two), lane f taking splits f, f + F, ...: a few loads per thread, all in
-  // flight together, a register-only combine with a running maximum, and the F
-  // partials combined across lanes.
-  int32_t* myflags = flags + mj * nsplit;
-  if (threadIdx.x == 0) s_ok = 1;
-  for (int t = threadIdx.x; t < nsplit; t += 256) {
-    if (t == split) continue;
-    int spins = 0;
-    while (__hip_atomic_load(myflags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && spins < kSpinLimit) {
-      __builtin_amdgcn_s_sleep(2);
-      ++spins;
-    }
-    if (spins >= kSpinLimit) s_ok = 0;
-  }
-  __syncthreads();
-  const int CK = (D / 4) / K;              // float4 columns of a head owned by this merger
-  const int P = Gc * CK;                   // (head, column) pairs, at most 256
-  int F = 1;                               // lanes per pair: largest power of two with P*F <= 256, at most 16
-  while (F < 16 && P * F * 2 <= 256) F *= 2;
-  const int t = threadIdx.x;
-  const int pr = t / F;
-  const int f = t & (F - 1);
-  const bool pv = pr < P;
-  const int ph = pv ? pr / CK : 0;
-  const int pc = mj * CK + pr % CK;
-  float Mr = -INFINITY;
-  float Lr = 0.f;
-  f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
-  if (pv) {
-    for (int s0 = f; s0 < nsplit; s0 += F * kMergeBatch) {
-      float2_t hm[kMergeBatch];
-      f32x4 v[kMergeBatch];
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int rec = min(s0 + u * F, nsplit - 1) * Gc + ph;
-        hm[u] = __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(rh, rec * 8, 0, kSc1));
-        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (rec * D + 4 * pc) * 4, 0, kSc1));
+      for (int w = 0; w < 4; ++w) {
+        sc[w] = __builtin_amdgcn_exp2f(red_m[w][col] - M);
+        L += red_l[w][col] * sc[w];
       }
-      // s0 < nsplit, so hm[0] is valid and mx is finite
-      float mx = Mr;
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) mx = fmaxf(mx, s0 + u * F < nsplit ? hm[u].x : -INFINITY);
-      const float sc = __builtin_amdgcn_exp2f(Mr - mx);
-      acc4 *= sc;
-      Lr *= sc;
-      Mr = mx;
+      for (int e = 0; e < E; ++e) {
+        float v = 0.f;
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const float e = __builtin_amdgcn_exp2f(hm[u].x - mx);
-        const float w = s0 + u * F < nsplit ? e : 0.f;
-        acc4 += v[u] * w;
-        Lr += hm[u].y * w;
+        for (int w = 0; w < 4; ++w) v += red_o[w][col][E * dl + e] * sc[w];
+        acc[e] = v;
       }
     }
-  }
-  // combine the F lanes of each pair (a lane that took no split holds m = -inf, l = 0)
-  float Mg = Mr;
-  for (int x = 1; x < F; x <<= 1) Mg = fmaxf(Mg, __shfl_xor(Mg, x));
-  const float w = Mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mr - Mg);
-  float Lg = Lr * w;
-  f32x4 o4 = acc4 * w;
-  for (int x = 1; x < F; x <<= 1) {
-    Lg += __shfl_xor(Lg, x);
+    if (nsplit == 1) {
+      if (hv2) {
+        const float inv = 1.f / L;
+        uint16_t* orow = out_row(ch, hh);
+        uint32_t w[E / 2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] += __shfl_xor(o4[e], x);
+        for (int e = 0; e < E / 2; ++e) w[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+        if constexpr (E == 8)
+          *reinterpret_cast<u32x4*>(orow + E * dl) = u32x4{w[0], w[1], w[2], w[3]};
+        else
+          *reinterpret_cast<u32x2*>(orow + E * dl) = u32x2{w[0], w[1]};
+      }
+      continue;
+    }
+
+    // Split records of this (sequence, kv head, column chunk): o rows
+    // [split][column in chunk][D] and (m, l) headers [split][column in chunk],
+    // written and read with device-scope (sc1) buffer accesses, which stay
+    // coherent across the XCDs' L2 caches.  The last K splits are also
+    // mergers: merger j combines output columns [j*D/K, (j+1)*D/K) of every
+    // column.  Flags: one row of nsplit per merger, so a merger clears its own
+    // row without racing another's wait.
+    const int K = nsplit >= kDecodeMergers ? kDecodeMergers : 2;   // divides D/4
+    const int mj = split - (nsplit - K);          // merger index, negative for the others
+    const int yrow = g * hchunks + hcb0 + ch;
+    const int64_t group = static_cast<int64_t>(a.split_off[b]) * gy + static_cast<int64_t>(yrow) * nsplit;
+    int32_t* flags = a.flags + group * kDecodeMergers;
+    const int gcc = Gc[ch];
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_o + group * (16 * D), 0, nsplit * gcc * D * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rh =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_h + group * (16 * 2), 0, nsplit * gcc * 2 * 4, kBufferWord3);
+    if (hv2) {
+      const int rec = split * gcc + hh;
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]}), ro,
+            (rec * D + E * dl + e) * 4, 0, kSc1);
+      if (dl == 0)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, float2_t{M, L}), rh, rec * 8, 0, kSc1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);        // this thread's record has reached the device
+    __syncthreads();                      // (also: the previous chunk's merge no longer reads s_ok)
+    if (static_cast<int>(threadIdx.x) < K && static_cast<int>(threadIdx.x) != mj)
+      __hip_atomic_store(flags + threadIdx.x * nsplit + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (mj < 0) continue;
+
+    // Merger: wait (bounded) for every other split's record.  Then each of this
+    // merger's (column, d-run) pairs is spread over F adjacent lanes (F a power
+    // of two), lane f taking splits f, f + F, ...: a few loads per thread, all
+    // in flight together, a register-only combine with a running maximum, and
+    // the F partials combined across lanes.
+    int32_t* myflags = flags + mj * nsplit;
+    if (threadIdx.x == 0) s_ok = 1;
+    __syncthreads();
+    for (int t = threadIdx.x; t < nsplit; t += 256) {
+      if (t == split) continue;
+      int spins = 0;
+      while (__hip_atomic_load(myflags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && spins < kSpinLimit) {
+        __builtin_amdgcn_s_sleep(2);
+        ++spins;
+      }
+      if (spins >= kSpinLimit) s_ok = 0;
+    }
+    __syncthreads();
+    const int CK = (D / 4) / K;              // float4 runs of a column owned by this merger
+    const int P = gcc * CK;                  // (column, run) pairs, at most 256
+    int F = 1;                               // lanes per pair: largest power of two with P*F <= 256, at most 16
+    while (F < 16 && P * F * 2 <= 256) F *= 2;
+    const int t = threadIdx.x;
+    const int pr = t / F;
+    const int f = t & (F - 1);
+    const bool pv = pr < P;
+    const int ph = pv ? pr / CK : 0;
+    const int pc = mj * CK + pr % CK;
+    float Mr = -INFINITY;
+    float Lr = 0.f;
+    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+    if (pv) {
+      for (int s0 = f; s0 < nsplit; s0 += F * kMergeBatch) {
+        float2_t hm[kMergeBatch];
+        f32x4 v[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const int rec = min(s0 + u * F, nsplit - 1) * gcc + ph;
+          hm[u] = __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(rh, rec * 8, 0, kSc1));
+          v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (rec * D + 4 * pc) * 4, 0, kSc1));
+        }
+        // s0 < nsplit, so hm[0] is valid and mx is finite
+        float mx = Mr;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) mx = fmaxf(mx, s0 + u * F < nsplit ? hm[u].x : -INFINITY);
+        const float sc = __builtin_amdgcn_exp2f(Mr - mx);
+        acc4 *= sc;
+        Lr *= sc;
+        Mr = mx;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const float e = __builtin_amdgcn_exp2f(hm[u].x - mx);
+          const float w = s0 + u * F < nsplit ? e : 0.f;
+          acc4 += v[u] * w;
+          Lr += hm[u].y * w;
+        }
+      }
+    }
+    // combine the F lanes of each pair (a lane that took no split holds m = -inf, l = 0)
+    float Mg = Mr;
+    for (int x = 1; x < F; x <<= 1) Mg = fmaxf(Mg, __shfl_xor(Mg, x));
+    const float w = Mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mr - Mg);
+    float Lg = Lr * w;
+    f32x4 o4 = acc4 * w;
+    for (int x = 1; x < F; x <<= 1) {
+      Lg += __shfl_xor(Lg, x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] += __shfl_xor(o4[e], x);
+    }
+    if (pv && f == 0) {
+      const float inv = s_ok ? 1.f / Lg : __builtin_nanf("");
+      uint16_t* orow = out_row(ch, ph);
+      *reinterpret_cast<u32x2*>(orow + 4 * pc) =
+          u32x2{pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv)};
+    }
+    // leave this merger's flag row at zero for the next call
+    for (int t2 = threadIdx.x; t2 < nsplit; t2 += 256)
+      if (t2 != split) __hip_atomic_store(myflags + t2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (pv && f == 0) {
-    const float inv = s_ok ? 1.f / Lg : __builtin_nanf("");
-    uint16_t* orow = out_row(ph);
-    *reinterpret_cast<u32x2*>(orow + 4 * pc) =
-        u32x2{pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv)};
-  }
-  // leave this merger's flag row at zero for the next call
-  for (int t = threadIdx.x; t < nsplit; t += 256)
-    if (t != split) __hip_atomic_store(myflags + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s) {
   const int hchunks = (a.ncol + 15) / 16;
   bool chunk = a.ncol != a.Hq / a.Hkv || a.n_rect != 1;
   for (int j = 0; j < a.nseq && !chunk; ++j) chunk = a.meta.count[j] != 1 || a.meta.row0[j] != 0;
-  const dim3 grid = chunk ? dim3(total_splits * hchunks * a.Hkv) : dim3(total_splits, a.Hkv * hchunks);
+  // chunk mode: two column chunks per workgroup
+  const dim3 grid = chunk ? dim3(total_splits * ((hchunks + 1) / 2) * a.Hkv) : dim3(total_splits, a.Hkv * hchunks);
   const bool win = a.window != 0;
   auto pick = [&](auto dv, auto cv, auto wv) {
     hipLaunchKernelGGL((decode_bf16_kernel<decltype(dv)::value, decltype(cv)::value, decltype(wv)::value>), grid,
