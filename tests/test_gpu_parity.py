@@ -362,6 +362,48 @@ def test_serving_decode_full_size_sampled():
     cache.close()
 
 
+def test_edit_full_size_sampled():
+    """Prompt edit at full size, in the call the benchmark times: 16 sequences of
+    4096 tokens (Hq=32 Hkv=8 d=128) prefilled, each truncated at its seeded edit
+    position m_b, then the suffix re-prefilled from new rows (the deep-layer case
+    of an edit).  The kept prefix [0, m_b) of every sequence must be byte-identical
+    before and after; sampled suffix rows of four sequences (the shortest and
+    longest kept prefixes among them) are compared with the oracle, and their
+    whole caches and block tables bit for bit."""
+    sh = W.EDIT
+    say(f"case: edit re-prefill, B={sh.B} n={sh.n} Hq={sh.Hq} Hkv={sh.Hkv} d={sh.d}, sampled rows")
+    full = W.prefill_inputs(sh, 1006)
+    ms = W.edit_points(sh.B, sh.n)
+    lens = [sh.n - m for m in ms]
+    suffix = W.prefill_inputs(W.AttnShape(B=sh.B, n=max(lens), Hq=sh.Hq, Hkv=sh.Hkv, d=sh.d, dtype=sh.dtype,
+                                          theta=sh.theta), 2006, lengths=lens, start=ms)
+    pair = Pair(1, sh.Hkv, sh.d, sh.B * (sh.n // 16) + 16, sh.B, sh.n // 16 + 2, sh.dtype, sh.theta,
+                max_position=sh.n + 32, free_order=W.page_order(sh.B * (sh.n // 16) + 16, 1006))
+    ids = list(range(sh.B))
+    pair.prefill(0, ids, full.Q, full.K, full.V, full.mask, full.positions, oracle=False)
+    before = [pair.gpu.gather(b, 0) for b in ids]
+    for b, m in zip(ids, ms):
+        pair.truncate(b, m)
+    Os, _ = pair.prefill(0, ids, suffix.Q, suffix.K, suffix.V, suffix.mask, suffix.positions, oracle=False)
+    Oc = Os.cpu()
+    for b, m in zip(ids, ms):
+        k, v = pair.gpu.gather(b, 0)
+        assert torch.equal(k[:, :m].view(torch.int16), before[b][0][:, :m].view(torch.int16)), f"prefix K of {b}"
+        assert torch.equal(v[:, :m].view(torch.int16), before[b][1][:, :m].view(torch.int16)), f"prefix V of {b}"
+    by_m = sorted(ids, key=lambda b: ms[b])
+    sample = [by_m[0], by_m[-1], by_m[len(by_m) // 2], 3]
+    worst = 0.0
+    for b in sample:
+        L = lens[b]
+        rows = sorted({0, 1, L // 2, L - 2, L - 1} & set(range(L)))
+        ref = pair.ref.prefill_rows(0, b, as_f32(suffix.Q[b, :, rows, :]), [ms[b] + r for r in rows])
+        _, rel = compare_rows(Oc[b, :, rows, :], ref, sh.dtype)
+        worst = max(worst, rel)
+        assert torch.all(Oc[b, :, L:, :] == 0), "padding rows of the suffix must be written as 0"
+    say(f"  worst row-relative error {worst:.3e}")
+    pair.check_cache(sample)
+
+
 def test_attention_half_matches_prefill():
     say("case: kv_cache_append + gqa_attention == gqa_prefill; rows inside a cached sequence")
     import causal_gqa_attention_attn_amd as lib
