@@ -274,20 +274,20 @@ def _sampled_prefill(shape, inp, order, rows, layers=1, seqs=None):
 
 
 def test_llama_full_size_sampled():
-    say("case: Llama-3-8B-shaped prefill B=8 n=2048 Hq=32 Hkv=8 d=128, permuted pages, sampled rows")
+    say("case: Llama-3-8B-shaped prefill B=8 n=2048 Hq=32 Hkv=8 d=128, permuted pages, sampled rows, 64 decode steps")
     inp = W.llama()
     B, n = 8, 2048
     order = W.page_order(B * (n // 16 + 4), 3003)
     rows = [0, 1, 31, 32, 63, 64, 1000, 2046, 2047]
     pair, worst = _sampled_prefill(W.LLAMA, inp, order, rows, seqs=[0, 7])
     say(f"  worst row-relative error {worst:.3e}")
-    for t in range(2):
+    # the 64 decode steps that follow the prefill: even steps append then decode,
+    # odd steps append and decode in one launch
+    for t in range(64):
         st = W.decode_step_inputs(W.LLAMA, 1003, t)
-        lens = [pair.ref.cache_length(s, 0) for s in range(B)]
-        pair.append(0, list(range(B)), st.k, st.v, torch.ones((B, 1), dtype=torch.uint8),
-                    torch.tensor([[x] for x in lens], dtype=torch.int32))
-        o, r = pair.decode(0, list(range(B)), st.q, [x + 1 for x in lens])
+        o, r = (pair.step_fused if t % 2 else pair.step)(0, list(range(B)), st)
         compare_rows(o, r, torch.bfloat16)
+    pair.check_cache([0, 7], invariants=False)
 
 
 def test_grok_full_size_sampled():
