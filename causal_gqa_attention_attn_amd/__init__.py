@@ -23,8 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgqa.so")
 
 if not os.path.exists(_LIB_PATH):
-    raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
-                      "or python causal_gqa_attention_attn_amd/build.py")
+    raise ImportError(f"{_LIB_PATH} is not built; run python causal_gqa_attention_attn_amd/build.py")
 
 _lib = ctypes.CDLL(_LIB_PATH)
 
