@@ -46,6 +46,8 @@
 //  * workgroups are dispatched heaviest (last) query tile first, kv head
 //    fastest, so with 8 kv heads workgroup i lands on XCD i % 8 = its kv head
 //    and each XCD's L2 serves one head's keys and values.
+#include <algorithm>
+
 #include "common.hpp"
 #include "device.hpp"
 
@@ -148,10 +150,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   const int zlo = a.meta.zlo[b], zhi = a.meta.zhi[b];
   const int h0 = g * G + hc * Gc;      // first query head of this workgroup
 
-  // padding rows of this workgroup's rectangular range -> 0 (after every
-  // page-table read, so those reads may use the scalar cache)
+  // padding rows of this entry's share [zlo, zhi) of the rectangle -> 0, Tq
+  // rows per query tile counted from zlo (after every page-table read, so
+  // those reads may use the scalar cache)
   auto zero_padding = [&]() {
-    const int rlo = tile * Tq;
+    const int rlo = zlo + tile * Tq;
     const int rhi = min(zhi, rlo + Tq);
     const int per_row = D / 8;
     for (int idx = threadIdx.x; idx < Gc * Tq * per_row; idx += 256) {
@@ -644,7 +647,11 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const PrefillShape ps = prefill_shape(G);
   const int Tq = 32 * ps.TB;
-  dim3 grid(a.Hkv * (G / ps.Gc), a.nseq, (a.n_rect + Tq - 1) / Tq);
+  // query tiles: enough for the longest share of rows (its run and the padding
+  // it zeroes), never more, so entries of short runs launch no idle tiles
+  int rows = 1;
+  for (int j = 0; j < a.nseq; ++j) rows = std::max(rows, a.meta.zhi[j] - a.meta.zlo[j]);
+  dim3 grid(a.Hkv * (G / ps.Gc), a.nseq, (rows + Tq - 1) / Tq);
   dim3 block(256);
   if (a.window) {
     if (a.d == 128)
