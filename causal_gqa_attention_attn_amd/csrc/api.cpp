@@ -446,8 +446,14 @@ gqa_status launch_attention(gqa_cache* c, int32_t layer, const int32_t* seq_ids,
   const gqa_cache_config& cf = c->cfg;
   const int64_t Hq = Q->shape[1];
   const int E = static_cast<int>(es.size());
-  for (int e0 = 0; e0 < E; e0 += kMaxSeqPerLaunch) {
-    const int nb = std::min(E - e0, kMaxSeqPerLaunch);
+  for (int e0 = 0, nb = 0; e0 < E; e0 += nb) {
+    // as many entries as fit one launch's entry and batch-row tables
+    int rows = 0;
+    for (nb = 0; e0 + nb < E && nb < gqa::kMaxRunsPerLaunch; ++nb) {
+      const bool new_row = nb == 0 || es[e0 + nb].b != es[e0 + nb - 1].b;
+      if (new_row && rows == gqa::kMaxRowsPerLaunch) break;
+      rows += new_row;
+    }
     gqa::AttnArgs a;
     std::memset(&a, 0, sizeof(a));
     a.Q = Q->data;
@@ -468,14 +474,19 @@ gqa_status launch_attention(gqa_cache* c, int32_t layer, const int32_t* seq_ids,
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
     a.pool_bytes = static_cast<uint32_t>(c->layer_elems * c->elt);
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    int rw = -1;
     for (int j = 0; j < nb; ++j) {
       const Entry& e = es[e0 + j];
-      a.meta.seq[j] = seq_ids[e.b];
-      a.meta.brow[j] = e.b;
+      if (j == 0 || e.b != es[e0 + j - 1].b) {
+        ++rw;
+        a.meta.seq[rw] = seq_ids[e.b];
+        a.meta.brow[rw] = e.b;
+        a.meta.total[rw] = total[e.b];
+      }
+      a.meta.row[j] = static_cast<uint8_t>(rw);
       a.meta.start[j] = e.start;
       a.meta.count[j] = e.count;
       a.meta.row0[j] = e.row0;
-      a.meta.total[j] = total[e.b];
       a.meta.zlo[j] = e.zlo;
       a.meta.zhi[j] = e.zhi;
     }
@@ -837,8 +848,8 @@ gqa_status launch_decode_f32(gqa_cache* c, int32_t layer, int32_t B, const int32
   const gqa_cache_config& cf = c->cfg;
   gqa_status st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
-  for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
-    const int nb = std::min(B - b0, kMaxSeqPerLaunch);
+  for (int b0 = 0; b0 < B; b0 += gqa::kMaxRowsPerLaunch) {
+    const int nb = std::min(B - b0, gqa::kMaxRowsPerLaunch);   // one entry per batch row
     gqa::AttnArgs a;
     std::memset(&a, 0, sizeof(a));
     a.Q = static_cast<const char*>(q->data) + b0 * q->stride[0] * c->elt;
@@ -858,6 +869,7 @@ gqa_status launch_decode_f32(gqa_cache* c, int32_t layer, int32_t B, const int32
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
     for (int j = 0; j < nb; ++j) {
+      a.meta.row[j] = static_cast<uint8_t>(j);
       a.meta.seq[j] = seq_ids[b0 + j];
       a.meta.brow[j] = j;
       a.meta.start[j] = T[b0 + j] - 1;

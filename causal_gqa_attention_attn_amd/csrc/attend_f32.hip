@@ -19,11 +19,11 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
   const int r = blockIdx.x * 64 + threadIdx.x;
   if (r >= a.n_rect) return;
   const int d = a.d;
-  const int seq = a.meta.seq[b];
+  const int seq = a.meta.seq[a.meta.row[b]];
   const int c0 = a.meta.start[b];
   const int nb = a.meta.count[b];
   const int r0 = a.meta.row0[b];
-  const int br = a.meta.brow[b];
+  const int br = a.meta.brow[a.meta.row[b]];
   float* orow = static_cast<float*>(a.O) + br * a.o_s0 + h * a.o_s1 + static_cast<int64_t>(r) * a.o_s2;
   if (r < r0 || r >= r0 + nb) {
     if (r >= a.meta.zlo[b] && r < a.meta.zhi[b])

@@ -9,6 +9,8 @@ namespace gqa {
 
 constexpr int kPage = 16;          // tokens per page
 constexpr int kMaxSeqPerLaunch = 64;
+constexpr int kMaxRunsPerLaunch = 144;   // entries of one attention launch
+constexpr int kMaxRowsPerLaunch = 32;    // batch rows of one attention launch
 constexpr int kMaxPatchPerLaunch = 240;
 constexpr int kMaxSplitDecode = 128;   // splits per sequence in one decode launch
 constexpr int kDecodeMergers = 4;      // splits of a sequence that combine the split records
@@ -35,6 +37,23 @@ struct SeqMeta {
   int32_t total[kMaxSeqPerLaunch];
   int32_t zlo[kMaxSeqPerLaunch];
   int32_t zhi[kMaxSeqPerLaunch];
+};
+
+// Entries of one attention launch, kept compact so that a row whose valid
+// tokens have many holes still fits few launches: per entry (a run of valid
+// rows) its first position, token count, first rectangular row, padding share
+// [zlo, zhi) and the index of its batch row in the per-row arrays; per batch
+// row its sequence, the batch row itself and the cache length read.
+struct AttnMeta {
+  int32_t start[kMaxRunsPerLaunch];
+  int32_t count[kMaxRunsPerLaunch];
+  int32_t row0[kMaxRunsPerLaunch];
+  int32_t zlo[kMaxRunsPerLaunch];
+  int32_t zhi[kMaxRunsPerLaunch];
+  uint8_t row[kMaxRunsPerLaunch];
+  int32_t seq[kMaxRowsPerLaunch];
+  int32_t brow[kMaxRowsPerLaunch];
+  int32_t total[kMaxRowsPerLaunch];
 };
 
 struct PatchArgs {
@@ -74,7 +93,7 @@ struct AttnArgs {
   float scale_log2;           // log2(e)/sqrt(d)
   uint32_t pool_bytes;        // bytes of this layer's K (= V) pool; offsets into it fit 32 bits
   const float* rope;
-  SeqMeta meta;
+  AttnMeta meta;              // nseq entries
 };
 
 struct DecodeArgs {

@@ -141,12 +141,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  const int seq = a.meta.seq[b];
+  const int rw = a.meta.row[b];
+  const int seq = a.meta.seq[rw];
   const int c0 = a.meta.start[b];
   const int nb = a.meta.count[b];
   const int r0 = a.meta.row0[b];
-  const int total = a.meta.total[b];
-  const int br = a.meta.brow[b];       // batch row of Q and O
+  const int total = a.meta.total[rw];
+  const int br = a.meta.brow[rw];      // batch row of Q and O
   const int zlo = a.meta.zlo[b], zhi = a.meta.zhi[b];
   const int h0 = g * G + hc * Gc;      // first query head of this workgroup
 
