@@ -157,3 +157,28 @@ def test_holey_chunk_with_workspace_takes_the_tiled_kernel():
     O, ref = pair.prefill(0, [0, 1], Q, K, V, mask, pos, workspace=pair.chunk_workspace(2, Hq, 8))
     _check(O, ref, mask, Hq, torch.bfloat16)
     pair.check_cache([0, 1])
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,d", [(torch.bfloat16, 8, 2, 64), (torch.float32, 4, 2, 32)])
+def test_many_rows_and_runs_span_launches(dtype, Hq, Hkv, d):
+    """70 batch rows, most with two or three runs of valid rows: more rows and
+    runs than one attention launch takes, so the entries are cut into several
+    launches; then a decode step over all 70 sequences."""
+    say(f"case: 70 rows with holes over several launches, {dtype} Hq={Hq} Hkv={Hkv} d={d}")
+    rng = np.random.default_rng(35)
+    B, n = 70, 40
+    rows = []
+    for b in range(B):
+        k = int(rng.integers(0, 4))
+        rows.append(sorted(rng.choice(n, size=int(rng.integers(1, n)), replace=False).tolist()) if k else
+                    list(range(int(rng.integers(1, n)))))
+    shape = W.AttnShape(B=B, n=n, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, theta=1e4)
+    pair = Pair(1, Hkv, d, B * 4, B, 4, dtype, 1e4, free_order=W.page_order(B * 4, 36))
+    ids = list(range(B))
+    Q, K, V, mask, pos = _holey(shape, 907, rows, [0] * B)
+    O, ref = pair.prefill(0, ids, Q, K, V, mask, pos)
+    _check(O, ref, mask, Hq, dtype)
+    pair.check_cache(ids)
+    o, r = pair.step(0, ids, W.decode_step_inputs(W.AttnShape(B=B, n=1, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype,
+                                                              theta=1e4), 908, 0))
+    compare_rows(o, r, dtype)
