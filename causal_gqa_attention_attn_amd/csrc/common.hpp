@@ -11,7 +11,7 @@ constexpr int kPage = 16;          // tokens per page
 constexpr int kMaxSeqPerLaunch = 64;
 constexpr int kMaxRunsPerLaunch = 144;   // entries of one attention launch
 constexpr int kMaxRowsPerLaunch = 64;    // batch rows of one attention launch (row index fits 8 bits)
-constexpr int kMaxPatchPerLaunch = 240;
+constexpr int kMaxPatchPerLaunch = 496;   // block-table entries (or page copies) per launch; the arguments stay under 4 KiB
 constexpr int kMaxSplitDecode = 128;   // splits per sequence in one decode launch
 constexpr int kDecodeMergers = 4;      // splits of a sequence that combine the split records
 
