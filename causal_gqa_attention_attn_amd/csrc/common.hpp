@@ -136,6 +136,14 @@ struct CopyArgs {
   int32_t dst[kMaxPatchPerLaunch];
 };
 
+// Every argument block stays within 4 KiB, the kernel-argument size every
+// launch path takes.
+static_assert(sizeof(AttnArgs) <= 4096, "attention arguments exceed 4 KiB");
+static_assert(sizeof(DecodeArgs) <= 4096, "decode arguments exceed 4 KiB");
+static_assert(sizeof(AppendArgs) <= 4096, "append arguments exceed 4 KiB");
+static_assert(sizeof(PatchArgs) <= 4096, "block-table patch arguments exceed 4 KiB");
+static_assert(sizeof(CopyArgs) <= 4096, "page copy arguments exceed 4 KiB");
+
 hipError_t launch_table_patch(const PatchArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int dtype, int grid_x, hipStream_t s);
 hipError_t launch_attend_f32(const AttnArgs& a, hipStream_t s);
