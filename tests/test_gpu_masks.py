@@ -182,3 +182,39 @@ def test_many_rows_and_runs_span_launches(dtype, Hq, Hkv, d):
     o, r = pair.step(0, ids, W.decode_step_inputs(W.AttnShape(B=B, n=1, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype,
                                                               theta=1e4), 908, 0))
     compare_rows(o, r, dtype)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,window", [(32, 8, 128, 0), (8, 2, 64, 0), (16, 4, 128, 48)])
+def test_short_runs_take_32_token_tiles(Hq, Hkv, d, window):
+    """Rows whose valid tokens come in runs of at most 32 (here 1 to 12 tokens
+    between padding): with 4 dividing Hq/Hkv the launch uses 32-token query
+    tiles of four heads.  Two such prefills continue each cache (the second
+    one's queries also see the first one's keys), with and without a window."""
+    say(f"case: runs of 1..12 tokens, bf16 Hq={Hq} Hkv={Hkv} d={d} window={window}")
+    rng = np.random.default_rng(37 + window)
+    B, n = 5, 150
+    shape = W.AttnShape(B=B, n=n, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4)
+    pages = B * 24
+    pair = Pair(1, Hkv, d, pages, B, 24, torch.bfloat16, 1e4, max_position=1024,
+                free_order=W.page_order(pages, 38), window=window)
+    ids = list(range(B))
+    lens = [0] * B
+
+    def fragmented():
+        rows_per_b = []
+        for b in range(B):
+            rows, r = [], int(rng.integers(0, 4))
+            while r < n:
+                k = int(rng.integers(1, 13))
+                rows.extend(range(r, min(n, r + k)))
+                r += k + int(rng.integers(1, 6))
+            rows_per_b.append(rows if b != 3 else rows[:1])
+        return rows_per_b
+
+    for rnd in range(2):
+        rows = fragmented()
+        Q, K, V, mask, pos = _holey(shape, 910 + rnd, rows, lens)
+        O, ref = pair.prefill(0, ids, Q, K, V, mask, pos)
+        _check(O, ref, mask, Hq, torch.bfloat16)
+        lens = [a + len(r) for a, r in zip(lens, rows)]
+    pair.check_cache(ids)
