@@ -634,14 +634,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
 // Heads per workgroup (Gc, dividing G) and 32-token blocks per workgroup (TB)
 // with Gc * TB = 4 (one row-block per wave) and TB >= 2: 64-token query tiles
 // match the 64-key tiles, which keeps the diagonal's masked work small.  When
-// every run of the launch has at most 32 tokens (a mask with many holes) and 4
-// divides G, 32-token tiles of four heads leave half as many rows idle.
+// 64-token tiles would leave more than an eighth of their rows idle (short or
+// ragged runs, masks with holes) and 4 divides G, 32-token tiles of four heads
+// are used instead.
 struct PrefillShape {
   int Gc, TB;
 };
 
-static PrefillShape prefill_shape(int G, int max_count) {
-  if (max_count <= 32 && G % 4 == 0) return {4, 1};
+static PrefillShape prefill_shape(int G, int64_t idle64, int64_t rows64) {
+  if (G % 4 == 0 && idle64 * 8 > rows64) return {4, 1};
   for (int Gc = 2; Gc >= 1; --Gc)
     if (G % Gc == 0) return {Gc, 4 / Gc};
   return {1, 4};
@@ -649,9 +650,13 @@ static PrefillShape prefill_shape(int G, int max_count) {
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  int max_count = 0;
-  for (int j = 0; j < a.nseq; ++j) max_count = std::max(max_count, a.meta.count[j]);
-  const PrefillShape ps = prefill_shape(G, max_count);
+  int64_t rows64 = 0, idle64 = 0;             // rows of 64-token tiles, and those without a query
+  for (int j = 0; j < a.nseq; ++j) {
+    const int64_t t64 = (a.meta.count[j] + 63) / 64 * 64;
+    rows64 += t64;
+    idle64 += t64 - a.meta.count[j];
+  }
+  const PrefillShape ps = prefill_shape(G, idle64, rows64);
   const int Tq = 32 * ps.TB;
   // query tiles: enough for the longest share of rows (its run and the padding
   // it zeroes), never more, so entries of short runs launch no idle tiles
