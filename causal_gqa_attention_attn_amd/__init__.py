@@ -9,7 +9,7 @@ the HIP kernels of the library; if ``libgqa.so`` is missing, importing this
 package raises ImportError (there is no fallback).
 
 ``PagedCache`` is a convenience owner of the caller-side device buffers (pools,
-block table, rotation table) allocated with torch.
+block table, rotation table) allocated with torch; it reads nothing back.
 """
 from __future__ import annotations
 
@@ -29,11 +29,12 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 F32, BF16 = 0, 1
 STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "MASK", -5: "POSITION",
-          -6: "CACHE", -7: "OUT_OF_PAGES", -8: "UNSUPPORTED", -9: "HIP"}
+          -6: "CACHE", -7: "OUT_OF_PAGES", -8: "UNSUPPORTED", -9: "HIP", -10: "DEVICE"}
 EXPORTS = ["gqa_cache_buffer_sizes", "gqa_cache_create", "gqa_cache_destroy", "kv_cache_append",
            "gqa_prefill", "gqa_attention", "gqa_decode", "gqa_decode_step", "kv_cache_truncate", "kv_cache_fork", "kv_cache_remap", "gqa_cache_length",
            "gqa_cache_page_table", "gqa_cache_free_pages", "gqa_cache_check", "gqa_workspace_size",
-           "gqa_attention_workspace_size", "gqa_prefix_index_create", "gqa_prefix_index_destroy",
+           "gqa_attention_workspace_size", "gqa_workspace_status", "gqa_set_merge_wait",
+           "gqa_prefix_index_create", "gqa_prefix_index_destroy",
            "gqa_prefix_index_insert", "gqa_prefix_index_remove", "gqa_prefix_index_match",
            "gqa_last_error"]
 
@@ -88,6 +89,8 @@ _sig = {
     "gqa_cache_check": [_P],
     "gqa_workspace_size": [_P, ctypes.c_int32, ctypes.c_int32],
     "gqa_attention_workspace_size": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
+    "gqa_workspace_status": [_P, _P, ctypes.c_size_t, ctypes.c_int32, _P],
+    "gqa_set_merge_wait": [ctypes.c_int32, ctypes.c_int32],
     "gqa_last_error": [],
 }
 for _name, _args in _sig.items():
@@ -300,6 +303,18 @@ def gqa_attention_workspace_size(handle, B, Hq, n) -> int:
     return int(_lib.gqa_attention_workspace_size(handle, B, Hq, n))
 
 
+def gqa_workspace_status(handle, workspace, clear=False, stream=None):
+    """Raises GqaError (GQA_ERR_DEVICE) if a split combine using this workspace
+    gave up since the status was last cleared; clear=True resets it after the read."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.gqa_workspace_status(handle, workspace.data_ptr(), nbytes, 1 if clear else 0, _stream(stream)),
+           "gqa_workspace_status")
+
+
+def gqa_set_merge_wait(polls, unreachable=False):
+    _check(_lib.gqa_set_merge_wait(polls, 1 if unreachable else 0), "gqa_set_merge_wait")
+
+
 def gqa_last_error() -> str:
     return _lib.gqa_last_error().decode()
 
@@ -341,51 +356,3 @@ class PagedCache:
             self.close()
         except Exception:
             pass
-
-    # views of the pools (logical layouts of include/gqa.h)
-    def k_view(self):
-        return self.k_pool.view(self.L, self.num_pages, self.Hkv, self.P, self.d)
-
-    def v_view(self):
-        return self.v_pool.view(self.L, self.num_pages, self.Hkv, self.d, self.P)
-
-    def gather(self, seq_id, layer):
-        """Logical (K_used, V) of one sequence and layer, [Hkv, len, d], gathered
-        through the library's block table (plain torch indexing, for tests)."""
-        n = gqa_cache_length(self.handle, seq_id, layer)
-        pages = gqa_cache_page_table(self.handle, seq_id)
-        if n == 0:
-            z = torch.zeros(self.Hkv, 0, self.d, dtype=self.dtype)
-            return z, z.clone()
-        idx = torch.tensor(pages, dtype=torch.long, device=self.k_pool.device)
-        k = self.k_view()[layer].index_select(0, idx)            # [np, Hkv, P, d]
-        v = self.v_view()[layer].index_select(0, idx)            # [np, Hkv, d, P]
-        k = k.permute(1, 0, 2, 3).reshape(self.Hkv, -1, self.d)[:, :n]
-        v = v.permute(1, 0, 3, 2).reshape(self.Hkv, -1, self.d)[:, :n]
-        return k.cpu(), v.cpu()
-
-    def gather_resident(self, seq_id, layer):
-        """(first, K_used, V) of the positions [first, len) a ring still holds
-        (first = 0 without a window): logical page L is read from table entry
-        L mod max_pages_per_seq."""
-        n = gqa_cache_length(self.handle, seq_id, layer)
-        if not self.window:
-            return (0,) + self.gather(seq_id, layer)
-        if n == 0:
-            z = torch.zeros(self.Hkv, 0, self.d, dtype=self.dtype)
-            return 0, z, z.clone()
-        R = self.max_pages_per_seq
-        pages = gqa_cache_page_table(self.handle, seq_id)
-        last = (n - 1) // self.P
-        first_page = max(0, last - R + 1)
-        idx = torch.tensor([pages[L % R] for L in range(first_page, last + 1)], dtype=torch.long,
-                           device=self.k_pool.device)
-        k = self.k_view()[layer].index_select(0, idx)
-        v = self.v_view()[layer].index_select(0, idx)
-        first = first_page * self.P
-        k = k.permute(1, 0, 2, 3).reshape(self.Hkv, -1, self.d)[:, :n - first]
-        v = v.permute(1, 0, 3, 2).reshape(self.Hkv, -1, self.d)[:, :n - first]
-        return first, k.cpu(), v.cpu()
-
-    def device_table(self, seq_id, count):
-        return self.page_table.view(-1, self.max_pages_per_seq)[seq_id, :count].cpu().tolist()

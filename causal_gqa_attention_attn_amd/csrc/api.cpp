@@ -12,7 +12,8 @@
 // Rules fixed by this library where the pages leave a choice:
 //  * slot = position: the valid tokens of a call must carry positions
 //    c, c+1, ... where c is the current length of that (sequence, layer);
-//  * the valid tokens of a row form one contiguous run;
+//  * the valid tokens of a row may have padding before, after and between
+//    them; each run of consecutive valid tokens is one launch entry;
 //  * a page serves every layer of its sequence; the first layer that needs a
 //    logical page takes it from the front of the free list, in batch order then
 //    logical-page order; truncation returns pages to the back in ascending
@@ -27,6 +28,7 @@
 //    copy-on-write);
 //  * every check runs before any state changes or any launch.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <deque>
@@ -691,30 +693,47 @@ GQA_EXPORT gqa_status gqa_attention(gqa_cache* c, int32_t layer, int32_t B, cons
 
 namespace {
 
-// Workspace of the split-T kernel, cut into slots of one (split, kv head x
-// column chunk) each: a ready-flag row of kDecodeMergers int32, 16 split o rows
-// of d float32 and 16 (m, l) headers.  The cut depends only on the workspace's
-// size and d, never on a call's shape, so calls of any B, Hq or chunk length
-// can share one workspace: the flags sit first and every call leaves them zero.
+// Workspace of the split-T kernel: a 256-byte header whose first word is the
+// sticky failure status, then slots of one (split, kv head x column chunk)
+// each: a ready-flag row of kDecodeMergers int32, 16 split o rows of d float32
+// and 16 (m, l) headers.  The cut depends only on the workspace's size and d,
+// never on a call's shape, so calls of any B, Hq or chunk length can share one
+// workspace: the flags sit first and every call leaves them zero.
+constexpr int64_t kWsHeader = 256;
+
 struct WsView {
+  int32_t* status = nullptr;
   int32_t* flags = nullptr;
   float* part_o = nullptr;
   float* part_h = nullptr;
   int64_t slots = 0;
+  int64_t zero_bytes = 0;    // header + flags: what a reset clears
 };
 
 int64_t ws_slot_bytes(int64_t d) { return (16 * d + 16 * 2 + gqa::kDecodeMergers) * 4; }
 
 WsView ws_view(void* ws, size_t bytes, int64_t d) {
   WsView v;
-  if (!ws || bytes < 256) return v;
-  v.slots = static_cast<int64_t>((bytes - 256) / ws_slot_bytes(d));
-  v.flags = static_cast<int32_t*>(ws);
+  if (!ws || bytes < static_cast<size_t>(2 * kWsHeader)) return v;
+  // the header and the 256-byte rounding of the flags fit in 2 * kWsHeader
+  v.slots = static_cast<int64_t>((bytes - 2 * kWsHeader) / ws_slot_bytes(d));
+  v.status = static_cast<int32_t*>(ws);
+  v.flags = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kWsHeader);
   const int64_t flag_bytes = ceil_div(v.slots * gqa::kDecodeMergers * 4, 256) * 256;
-  v.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + flag_bytes);
+  v.zero_bytes = kWsHeader + flag_bytes;
+  v.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + v.zero_bytes);
   v.part_h = v.part_o + v.slots * 16 * d;
   return v;
 }
+
+// Ready-flag values: every launch takes a fresh nonzero epoch (a flag left by
+// a launch whose merge gave up never equals a later launch's).  The merge wait
+// and a test control that makes it give up are process-wide.
+std::atomic<uint32_t> g_epoch{0};
+std::atomic<int32_t> g_spin_limit{1 << 18};
+std::atomic<int32_t> g_unreachable{0};
+
+int32_t next_epoch() { return static_cast<int32_t>(g_epoch.fetch_add(1) % 0x3fffffffu) + 1; }
 
 // (kv head x column chunk) rows of the grid for ncol (token, head) columns
 int64_t split_ys(const gqa_cache* c, int64_t ncol) { return c->cfg.num_kv_heads * ceil_div(ncol, 16); }
@@ -752,7 +771,7 @@ int64_t split_count(int32_t T, int pps) { return std::max<int64_t>(1, ceil_div(c
 // most ceil(target / ys) + B.
 size_t ws_bytes_for(const gqa_cache* c, int64_t B, int64_t ys) {
   const int64_t slots = (ceil_div(kDecodeTargetBlocks, ys) + B) * ys;
-  return static_cast<size_t>(256 + slots * ws_slot_bytes(c->cfg.head_dim));
+  return static_cast<size_t>(2 * kWsHeader + slots * ws_slot_bytes(c->cfg.head_dim));
 }
 
 // Split-T attention over the paged cache for short query runs (one launch per
@@ -810,7 +829,11 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
       a.part_o = wv.part_o + split_base * ys * 16 * cf.head_dim;
       a.part_h = wv.part_h + split_base * ys * 16 * 2;
       a.flags = wv.flags + split_base * ys * gqa::kDecodeMergers;
+      a.status = wv.status;
     }
+    a.epoch = next_epoch();
+    a.wait_value = g_unreachable.load() ? (a.epoch ^ 0x40000000) : a.epoch;
+    a.spin_limit = g_spin_limit.load();
     int32_t off = 0;
     for (int j = 0; j < nb; ++j) {
       const int b = b0 + j;
@@ -974,6 +997,35 @@ GQA_EXPORT size_t gqa_workspace_size(const gqa_cache* c, int32_t B, int32_t Hq) 
 GQA_EXPORT size_t gqa_attention_workspace_size(const gqa_cache* c, int32_t B, int32_t Hq, int32_t n) {
   if (!c || B < 0 || Hq < 1 || n < 1 || n > GQA_MAX_CHUNK_TOKENS || c->cfg.dtype != GQA_BF16) return 0;
   return ws_bytes_for(c, B, split_ys(c, static_cast<int64_t>(n) * std::max(1, Hq / c->cfg.num_kv_heads)));
+}
+
+GQA_EXPORT gqa_status gqa_workspace_status(const gqa_cache* c, void* workspace, size_t ws_bytes, int32_t clear,
+                                           void* stream) {
+  if (!c) return fail(GQA_ERR_ARG, "cache is null");
+  const WsView wv = ws_view(workspace, ws_bytes, c->cfg.head_dim);
+  if (!wv.slots) return fail(GQA_ERR_ARG, "workspace missing or smaller than one slot");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, wv.status, sizeof(word), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "workspace status read");
+  if (clear) {
+    e = hipMemsetAsync(workspace, 0, static_cast<size_t>(wv.zero_bytes), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "workspace reset");
+  }
+  if (word)
+    return fail(GQA_ERR_DEVICE,
+                "a split merge gave up waiting for a split: some output written since the last clear holds NaN");
+  return GQA_OK;
+}
+
+GQA_EXPORT gqa_status gqa_set_merge_wait(int32_t polls, int32_t unreachable) {
+  if (polls < 0) return fail(GQA_ERR_ARG, "polls must be >= 0");
+  g_spin_limit.store(polls);
+  g_unreachable.store(unreachable ? 1 : 0);
+  return GQA_OK;
 }
 
 GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,

@@ -119,6 +119,10 @@ struct DecodeArgs {
   float* part_o;              // split o rows [split][y][16][d]
   float* part_h;              // split (m, l) headers [split][y][16][2]
   int32_t* flags;             // ready flags [split group][merger][split]; zero between calls
+  int32_t* status;            // sticky failure word of the workspace (set when a merge gives up)
+  int32_t epoch;              // nonzero value a split writes into its ready flags for this call
+  int32_t wait_value;         // flag value the mergers wait for (epoch, unless a test forces a give-up)
+  int32_t spin_limit;         // polls of one ready flag before a merger gives up
   int32_t split_off[kMaxSeqPerLaunch + 1];
   SeqMeta meta;               // start: position of the first query token; count: query tokens;
                               // row0: their first rectangular row; total: keys read (start + count)

@@ -37,7 +37,11 @@
 //    only wait on workgroups dispatched before them or on each other, and
 //    there are never more of them than the chip holds at once.  Each polls its
 //    flags with a bounded spin, combines its share of the output columns and
-//    clears its own flag row for the next call.
+//    clears its own flag row for the next call.  A split writes the call's
+//    epoch (a nonzero number the host changes from call to call) as its flag,
+//    so a flag left by an earlier call that gave up never passes for a new
+//    one; a merger that gives up writes NaN and sets the workspace's sticky
+//    status word, which the host reads back as an error.
 #include "common.hpp"
 #include "device.hpp"
 
@@ -48,7 +52,6 @@ namespace {
 #ifndef GQA_DECODE_BATCH
 #define GQA_DECODE_BATCH 2                 // pages a wave keeps in flight
 #endif
-constexpr int kSpinLimit = 1 << 18;        // bounded wait for a split's flag
 constexpr int kMergeBatch = 8;             // split records a merging thread loads at once
 constexpr int kSc1 = 16;                   // buffer cache policy: sc1 (device-scope coherent)
 constexpr int kBufferWord3 = 0x00020000;   // buffer resource word 3: raw 32-bit dword access
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);        // this thread's record has reached the device
     __syncthreads();                      // (also: the previous chunk's merge no longer reads s_ok)
     if (static_cast<int>(threadIdx.x) < K && static_cast<int>(threadIdx.x) != mj)
-      __hip_atomic_store(flags + threadIdx.x * nsplit + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(flags + threadIdx.x * nsplit + split, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (mj < 0) continue;
 
     // Merger: wait (bounded) for every other split's record.  Then each of this
@@ -479,13 +482,17 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
     for (int t = threadIdx.x; t < nsplit; t += 256) {
       if (t == split) continue;
       int spins = 0;
-      while (__hip_atomic_load(myflags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 && spins < kSpinLimit) {
+      while (__hip_atomic_load(myflags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.wait_value) {
+        if (spins >= a.spin_limit) {
+          s_ok = 0;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
         ++spins;
       }
-      if (spins >= kSpinLimit) s_ok = 0;
     }
     __syncthreads();
+    if (threadIdx.x == 0 && !s_ok) __hip_atomic_store(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int CK = (D / 4) / K;              // float4 runs of a column owned by this merger
     const int P = gcc * CK;                  // (column, run) pairs, at most 256
     int F = 1;                               // lanes per pair: largest power of two with P*F <= 256, at most 16

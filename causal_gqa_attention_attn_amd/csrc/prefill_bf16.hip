@@ -35,9 +35,10 @@
 //    loop keeps no running maximum and never rescales; the probabilities are
 //    rounded to bf16 once, and their row sums are taken from those bf16 values
 //    with dot2 instructions.  A row whose sum passes 2^64 (some score beyond
-//    the reference by more than 2^64 in probability) makes the workgroup find
-//    the exact row maxima in a score-only pass and run again against them,
-//    which cannot overflow;
+//    the reference by more than 2^64 in probability) or stays below 1/2 (no
+//    visible key at the reference) makes the workgroup find the exact row
+//    maxima in a score-only pass and run again against them, which can
+//    neither overflow nor underflow;
 //  * key tiles wholly in the future of the workgroup are never loaded;
 //    masking by select happens only on tiles that cross the diagonal;
 //  * value slots at or beyond the written length are zeroed in LDS by the
@@ -494,9 +495,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
         mx = fmaxf(mx, key <= qpos ? sA[0][i] : -INFINITY);
       }
     } else {
-      // reference: maximum of the row's visible keys among the first two key
-      // tiles read, which hold every row's first visible key (the rows of a
-      // workgroup start their windows less than 64 keys apart)
+      // reference: maximum of the row's visible keys among the key tiles that
+      // hold its first visible key.  A row's window starts at most Tq - 1
+      // keys after the first row's, so with 64-token query tiles the first
+      // two tiles read hold every row's first visible key, and with 128-token
+      // tiles the first three do (the third is taken below when some row needs it)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -515,11 +518,27 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
           }
       }
     }
+    __syncthreads();                         // K(0) is read by every wave before K(2) replaces it
+    if (ntk > 2) issue_k(p2, 0);
+    if constexpr (WIN) {
+      // the last row's window starts at or past key tile kt0 + 2: wait for
+      // K(2) and take its visible keys too (step 0 overwrites sB again)
+      if (ntk > 2 && c0 + t0 + qn - a.window >= (kt0 + 2) * KT) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        qk(ks[0], sB);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = (kt0 + 2) * KT + sub * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
+            mx = fmaxf(mx, key <= qpos && key > qpos - a.window ? sB[sub][i] : -INFINITY);
+          }
+      }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     if (WIN && mx == -INFINITY) mx = 0.f;    // padding lanes only
     mneg = -(mx * sl2);
-    __syncthreads();                         // K(0) is read by every wave before K(2) replaces it
-    if (ntk > 2) issue_k(p2, 0);
   }
   // leading tiles wholly visible to the whole workgroup (each with a next
   // tile) in pairs, then the rest with masks
@@ -567,10 +586,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
 
   // A row whose sum passed 2^64 (or is not finite) had a score far above its
   // reference: find the exact row maxima (scores only) and run once more,
-  // one tile at a time, against them.
+  // one tile at a time, against them.  A reference taken from one of the
+  // row's visible keys gives that key the probability 1, so a sum below 1/2
+  // means the reference missed the row's keys: the same pass handles it.
   float l = l0 + l1;
   float l_tot = l + __shfl_xor(l, 32);
-  if (__syncthreads_or(q_ok && !(l_tot <= 0x1p64f))) {
+  if (__syncthreads_or(q_ok && !(l_tot >= 0.5f && l_tot <= 0x1p64f))) {
     float m = -INFINITY;
     for (int kt = 0; kt < ntk; ++kt) {
       int pid = page_id(kt), unused = 0;

@@ -47,12 +47,13 @@ typedef enum gqa_status {
   GQA_ERR_ARG = -1,          /* null pointer, out-of-range id, repeated sequence   */
   GQA_ERR_SHAPE = -2,        /* tensor shape/stride/alignment, Hkv does not divide Hq */
   GQA_ERR_DTYPE = -3,        /* tensor dtype differs from the cache dtype          */
-  GQA_ERR_MASK = -4,         /* mask entry not 0/1, or valid tokens not contiguous */
+  GQA_ERR_MASK = -4,         /* mask entry not 0 or 1                              */
   GQA_ERR_POSITION = -5,     /* positions do not continue the cache ([P1] 2.11)    */
   GQA_ERR_CACHE = -6,        /* cache state violated (lengths, pages in use)       */
   GQA_ERR_OUT_OF_PAGES = -7, /* page pool or a sequence's block table is full      */
   GQA_ERR_UNSUPPORTED = -8,  /* configuration outside what the kernels implement   */
-  GQA_ERR_HIP = -9           /* a HIP runtime call failed                          */
+  GQA_ERR_HIP = -9,          /* a HIP runtime call failed                          */
+  GQA_ERR_DEVICE = -10       /* a kernel reported a failure (gqa_workspace_status) */
 } gqa_status;
 
 typedef enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
@@ -134,8 +135,11 @@ gqa_status gqa_cache_buffer_sizes(const gqa_cache_config* cfg, size_t* k_pool_by
                                   size_t* v_pool_bytes, size_t* page_table_bytes,
                                   size_t* rope_table_bytes);
 
-/* Create the host-side state of a cache over caller-owned device buffers.
- * free_list_order: NULL for 0..num_pages-1, else a permutation of the pool that
+/* Create the host-side state of a cache over caller-owned device buffers
+ * ([P1] 2.5 LayerCache: per layer the used K and V with the lengths and
+ * layout metadata that locate each sequence's slots; [P3] PagedAttention
+ * lesson: a pool of fixed-size blocks, a per-request block table and free
+ * blocks handed out on demand).  free_list_order: NULL for 0..num_pages-1, else a permutation of the pool that
  * fixes the order in which free pages are handed out.  Page contents are not
  * touched (fresh pages may hold anything; nothing beyond a sequence's length
  * is ever used).  The rotation table is computed on the host here and copied to
@@ -144,6 +148,8 @@ gqa_status gqa_cache_buffer_sizes(const gqa_cache_config* cfg, size_t* k_pool_by
 gqa_status gqa_cache_create(const gqa_cache_config* cfg, void* k_pool, void* v_pool,
                             int32_t* page_table, void* rope_table,
                             const int32_t* free_list_order, gqa_cache** out);
+/* Release the host-side state ([P1] 2.5 LayerCache).  The device buffers stay
+ * the caller's; no HIP call is made.  NULL is accepted. */
 gqa_status gqa_cache_destroy(gqa_cache* cache);
 
 /* Append the valid tokens of K and V to layer `layer` of sequences seq_ids[0..B)
@@ -206,7 +212,10 @@ gqa_status gqa_attention(gqa_cache* cache, int32_t layer, int32_t B, const int32
  * layout depends only on ws_bytes and d).  Calls that share a workspace must
  * not overlap in time.  It may be NULL when every sequence fits one split
  * (short caches).  GQA_ERR_ARG if it is needed and missing, misaligned or too
- * small. */
+ * small.  The splits of a sequence are combined inside the launch; a combine
+ * that waits too long for a split (it never should) writes NaN to its outputs
+ * and sets the workspace's sticky status word, which gqa_workspace_status
+ * turns into GQA_ERR_DEVICE. */
 gqa_status gqa_decode(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
                       const gqa_tensor* q, const int32_t* valid_lengths, const gqa_tensor* o,
                       void* workspace, size_t ws_bytes, void* stream);
@@ -278,7 +287,18 @@ gqa_status gqa_prefix_index_match(const gqa_prefix_index* index, const int32_t* 
 gqa_status kv_cache_remap(gqa_cache* cache, int32_t n, const int32_t* src_pages,
                           const int32_t* dst_pages, void* stream);
 
-/* Host-side queries. */
+/* Host-side queries, no HIP call.
+ * gqa_cache_length: the written length of (seq_id, layer), i.e. the number of
+ *   slots [0, length) holding that layer's used K/V ([P1] 2.5: the cache
+ *   length equals the next position to write).  GQA_ERR_ARG for a null
+ *   argument or an id out of range.
+ * gqa_cache_page_table: the sequence's block table ([P3] PagedAttention
+ *   lesson: logical block t/16 of the sequence lives in physical page out[t/16];
+ *   in a ring, logical page L in entry L mod max_pages_per_seq).  *n_out gets
+ *   the number of entries; they are copied to the host array out[0..cap) when
+ *   they fit (GQA_ERR_ARG otherwise, with *n_out still set; out may be NULL
+ *   when the table is empty).
+ * gqa_cache_free_pages: pages on the free list. */
 gqa_status gqa_cache_length(const gqa_cache* cache, int32_t seq_id, int32_t layer, int32_t* out);
 gqa_status gqa_cache_page_table(const gqa_cache* cache, int32_t seq_id, int32_t* out, int32_t cap,
                                 int32_t* n_out);
@@ -301,6 +321,27 @@ size_t gqa_workspace_size(const gqa_cache* cache, int32_t B, int32_t Hq);
  * n < 1 or n > GQA_MAX_CHUNK_TOKENS) or for invalid arguments.  A workspace of
  * this size also serves gqa_decode for the same B and Hq. */
 size_t gqa_attention_workspace_size(const gqa_cache* cache, int32_t B, int32_t Hq, int32_t n);
+
+/* Sticky failure status of a split-T workspace.  Waits for the work queued on
+ * `stream`, then reads the status word that a split combine sets when it gives
+ * up waiting for a split (its outputs then hold NaN instead of a result).
+ * Returns GQA_OK if no combine has given up since the word was last cleared,
+ * GQA_ERR_DEVICE if one has.  With clear != 0 the word and every ready flag
+ * are zeroed afterwards (on `stream`, waited for), which makes the workspace
+ * as good as freshly zero-filled: do this after GQA_ERR_DEVICE before reusing
+ * it.  GQA_ERR_ARG for a null cache or a workspace too small for one slot;
+ * GQA_ERR_HIP if the read fails.  Synchronises: not for use under capture. */
+gqa_status gqa_workspace_status(const gqa_cache* cache, void* workspace, size_t ws_bytes, int32_t clear,
+                                void* stream);
+
+/* Test control of the split combine's bounded wait (process-wide, for tests of
+ * the failure report above).  polls: how many times a combine polls one ready
+ * flag before it gives up (default 262144, about 0.1 s); unreachable != 0
+ * makes combines wait for a flag value no split writes, so every split-T
+ * launch that needs a combine gives up after `polls` polls and reports it,
+ * while every workgroup still exits.  gqa_set_merge_wait(262144, 0) restores
+ * the default.  GQA_ERR_ARG if polls < 0.  Host only. */
+gqa_status gqa_set_merge_wait(int32_t polls, int32_t unreachable);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* gqa_last_error(void);

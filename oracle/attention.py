@@ -116,14 +116,19 @@ def attend_positions(q_used, q_pos, k_used, v, row_chunk: int = 1024, window: in
     (only the latest ``window`` of them when window > 0).
 
     Rows are independent, so they are evaluated ``row_chunk`` at a time only to
-    bound memory; each row's arithmetic is the same as in ``attend``.
+    bound memory; each row's arithmetic is the same as in ``attend``.  A chunk
+    only takes the slots that some row of it can see, [lo, hi): every slot
+    outside them has M = -inf for every row of the chunk, so it carries zero
+    weight and adds nothing to a row's maximum or denominator (section 2.2).
     """
     q_used = np.asarray(q_used, dtype=np.float64)
     q_pos = np.asarray(q_pos, dtype=np.int64)
-    T = np.asarray(k_used).shape[1]
     out = np.zeros(q_used.shape)
     for r0 in range(0, q_used.shape[1], row_chunk):
         r1 = min(q_used.shape[1], r0 + row_chunk)
-        M = window_mask(q_pos[r0:r1], T, window) if window else slot_mask(q_pos[r0:r1], T)
-        out[:, r0:r1] = attend(q_used[:, r0:r1], k_used, v, M)
+        p = q_pos[r0:r1]
+        hi = int(p.max()) + 1
+        lo = max(0, int(p.min()) - window + 1) if window else 0
+        M = window_mask(p - lo, hi - lo, window) if window else slot_mask(p, hi)
+        out[:, r0:r1] = attend(q_used[:, r0:r1], k_used[:, lo:hi], v[:, lo:hi], M)
     return out

@@ -107,7 +107,7 @@ def test_workspace_size_queries():
     slot = (16 * 128 + 32 + 4) * 4          # flag row, 16 o rows of d floats, 16 (m, l) headers
     for B, Hq, n in [(1, 32, 1), (4, 32, 4), (4, 64, 16), (3, 8, 7)]:
         ys = 8 * -(-(n * (Hq // 8)) // 16)   # kv heads x 16-column chunks
-        want = 256 + (-(-4096 // ys) + B) * ys * slot
+        want = 512 + (-(-4096 // ys) + B) * ys * slot   # status header, flag rounding, slots
         assert lib.gqa_attention_workspace_size(h, B, Hq, n) == want, (B, Hq, n)
         assert lib.gqa_attention_workspace_size(h, B, Hq, n) >= lib.gqa_workspace_size(h, B, Hq)
     lib.gqa_cache_destroy(h)
@@ -191,4 +191,24 @@ def test_rejections_match_oracle_without_gpu():
     lib.kv_cache_fork(h, 0, 1, 0)
     lib.gqa_cache_check(h)
     assert lib.gqa_cache_free_pages(h) == 4 and lib.gqa_cache_page_table(h, 1) == []
+    lib.gqa_cache_destroy(h)
+
+
+def test_failure_report_controls_validate_on_host():
+    """The split-combine status query and its test control reject bad arguments
+    before touching the device."""
+    import causal_gqa_attention_attn_amd as lib
+    with pytest.raises(lib.GqaError) as e:
+        lib.gqa_set_merge_wait(-1)
+    assert e.value.name == "ARG"
+    lib.gqa_set_merge_wait(1 << 18, False)          # the default, restored
+    st, h = _cache(lib)
+    assert st == 0
+    ws = torch.zeros(16, dtype=torch.uint8)         # smaller than the header and one slot
+    with pytest.raises(lib.GqaError) as e:
+        lib.gqa_workspace_status(h, ws)
+    assert e.value.name == "ARG"
+    with pytest.raises(lib.GqaError) as e:
+        lib.gqa_workspace_status(None, ws)
+    assert e.value.name == "ARG"
     lib.gqa_cache_destroy(h)

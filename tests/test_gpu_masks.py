@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads as W
-from harness import Pair, as_f32, compare_rows
+from harness import Pair, as_f32, compare_rows, gather
 
 pytestmark = pytest.mark.gpu
 
@@ -134,7 +134,7 @@ def test_padding_placement_gives_identical_outputs():
         pair = Pair(1, Hkv, d, 16, 1, 16, torch.bfloat16, 5e5)
         O, _ = pair.prefill(0, [0], Q, K, V, mask, pos, oracle=False)
         outs.append(O[0][:, rows].cpu())
-        caches.append(pair.gpu.gather(0, 0))
+        caches.append(gather(pair.gpu, 0, 0))
         pad = [i for i in range(n) if i not in rows]
         assert np.all(as_f32(O[0][:, pad]) == 0.0)
     for o, (k, v) in zip(outs[1:], caches[1:]):

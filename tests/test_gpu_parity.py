@@ -2,9 +2,10 @@
 
 Cache contents and block tables are compared bit for bit, outputs within
 1e-5 absolute (float32) or 2e-2 of the row maximum (bfloat16).  Small shapes
-span several tiles and ragged tails; full-size shapes (the Llama-3-8B- and
-Grok-1-shaped prefills, the 64-sequence serving decode) are checked on sampled
-rows that the oracle computes one by one.
+span several tiles and ragged tails; the full-size shapes (the Llama-3-8B- and
+Grok-1-shaped prefills, the 64-sequence serving decode, the 16-sequence edit)
+are checked on every output row, with the oracle's rows spread over a thread
+pool.
 """
 import sys
 
@@ -13,7 +14,11 @@ import pytest
 import torch
 
 import workloads as W
-from harness import Pair, as_f32, compare_rows
+from concurrent.futures import ThreadPoolExecutor
+
+from threadpoolctl import threadpool_limits
+
+from harness import Pair, as_f32, compare_rows, gather, k_view, oracle_rows, oracle_workers, v_view
 from test_oracle_pins import read_golden
 
 pytestmark = pytest.mark.gpu
@@ -143,7 +148,7 @@ def test_incremental_prefill_and_edit():
     pair.check_cache(ids)
     prefix = {}
     for s, m in zip(ids, ms):
-        prefix[s] = [pair.gpu.gather(s, l) for l in range(2)]
+        prefix[s] = [gather(pair.gpu, s, l) for l in range(2)]
         pair.truncate(s, m)
     lens = [n - m for m in ms]
     suffix = W.prefill_inputs(W.AttnShape(B=B, n=max(lens), Hq=32, Hkv=8, d=128,
@@ -156,7 +161,7 @@ def test_incremental_prefill_and_edit():
     pair.check_cache(ids)
     for s, m in zip(ids, ms):
         for l in range(2):
-            k, v = pair.gpu.gather(s, l)
+            k, v = gather(pair.gpu, s, l)
             k0, v0 = prefix[s][l]
             assert torch.equal(k[:, :m].view(torch.int16), k0[:, :m].view(torch.int16)), "prefix K changed"
             assert torch.equal(v[:, :m].view(torch.int16), v0[:, :m].view(torch.int16)), "prefix V changed"
@@ -216,8 +221,8 @@ def test_cached_decode_equals_full_recompute_gpu():
                  torch.tensor([[t]], dtype=torch.int32))
     b = Pair(1, 2, 64, 16, 1, 8, torch.bfloat16, 1e4)
     b.prefill(0, [0], inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
-    ka, va = a.gpu.gather(0, 0)
-    kb, vb = b.gpu.gather(0, 0)
+    ka, va = gather(a.gpu, 0, 0)
+    kb, vb = gather(b.gpu, 0, 0)
     assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
     assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
     a.check_cache([0])
@@ -253,49 +258,65 @@ def test_errors_match_oracle_gpu():
     lib.gqa_cache_check(pair.gpu.handle)
 
 
-# ------------------------------------------------------------------ full sizes, sampled rows
+# ------------------------------------------------------------------ full sizes, every row
 
-def _sampled_prefill(shape, inp, order, rows, layers=1, seqs=None):
-    B = shape.B
-    pages_per_seq = -(-shape.n // 16) + 4
-    pair = Pair(layers, shape.Hkv, shape.d, B * pages_per_seq, B, pages_per_seq, shape.dtype,
-                shape.theta, free_order=order)
-    ids = list(range(B))
-    O, _ = pair.prefill(0, ids, inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
+def _all_rows(pair, O, inp, seqs, layer=0, starts=None):
+    """Every valid row of every listed sequence against the oracle (threaded
+    over row blocks); returns the worst row-relative error."""
     Oc = O.cpu()
+    jobs, keep = [], []
+    for b in seqs:
+        nb = int(inp.mask[b].sum())
+        c = 0 if starts is None else starts[b]
+        jobs.append((b, as_f32(inp.Q[b, :, :nb, :]), np.arange(c, c + nb)))
+        keep.append(nb)
+    refs = oracle_rows(pair.ref, layer, jobs)
     worst = 0.0
-    for b in (seqs if seqs is not None else ids):
-        q_rows = as_f32(inp.Q[b, :, rows, :])
-        ref = pair.ref.prefill_rows(0, b, q_rows, rows)
-        _, rel = compare_rows(Oc[b, :, rows, :], ref, shape.dtype)
+    for b, nb, ref in zip(seqs, keep, refs):
+        _, rel = compare_rows(Oc[b, :, :nb, :], ref, torch.bfloat16)
         worst = max(worst, rel)
-    pair.check_cache(seqs if seqs is not None else ids, invariants=layers == 1)
-    return pair, worst
+        assert torch.all(Oc[b, :, nb:, :] == 0), f"padding rows of sequence {b} must be written as 0"
+    return worst
 
 
-def test_llama_full_size_sampled():
-    say("case: Llama-3-8B-shaped prefill B=8 n=2048 Hq=32 Hkv=8 d=128, permuted pages, sampled rows, 64 decode steps")
+def test_llama_full_size():
+    """Llama-3-8B-shaped prefill (B=8, n=2048, Hq=32, Hkv=8, d=128, permuted
+    page pool): every output row of all 8 sequences, every cache byte and block
+    table, then the 64 decode steps on all 8."""
+    say("case: Llama-3-8B-shaped prefill B=8 n=2048 Hq=32 Hkv=8 d=128, permuted pages, every row, 64 decode steps")
     inp = W.llama()
     B, n = 8, 2048
-    order = W.page_order(B * (n // 16 + 4), 3003)
-    rows = [0, 1, 31, 32, 63, 64, 1000, 2046, 2047]
-    pair, worst = _sampled_prefill(W.LLAMA, inp, order, rows, seqs=[0, 7])
-    say(f"  worst row-relative error {worst:.3e}")
+    pps = n // 16 + 4
+    order = W.page_order(B * pps, 3003)
+    pair = Pair(1, 8, 128, B * pps, B, pps, torch.bfloat16, 5e5, free_order=order)
+    ids = list(range(B))
+    O, _ = pair.prefill(0, ids, inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
+    worst = _all_rows(pair, O, inp, ids)
+    say(f"  worst row-relative error {worst:.3e} over {B * 32 * n} rows")
+    pair.check_cache(ids)
     # the 64 decode steps that follow the prefill: even steps append then decode,
     # odd steps append and decode in one launch
     for t in range(64):
         st = W.decode_step_inputs(W.LLAMA, 1003, t)
-        o, r = (pair.step_fused if t % 2 else pair.step)(0, list(range(B)), st)
+        o, r = (pair.step_fused if t % 2 else pair.step)(0, ids, st)
         compare_rows(o, r, torch.bfloat16)
-    pair.check_cache([0, 7], invariants=False)
+    pair.check_cache(ids)
+    pair.lib.gqa_workspace_status(pair.gpu.handle, pair.ws)
 
 
-def test_grok_full_size_sampled():
-    say("case: Grok-1-shaped prefill B=1 n=8192 Hq=48 Hkv=8 d=128, sampled rows; decode at T=8192")
+def test_grok_full_size():
+    """Grok-1-shaped prefill (B=1, n=8192, Hq=48, Hkv=8, d=128): all 8192 x 48
+    output rows and the whole cache; then a second layer of 8191 tokens, one
+    appended token and a decode at T=8192."""
+    say("case: Grok-1-shaped prefill B=1 n=8192 Hq=48 Hkv=8 d=128, every row; decode at T=8192")
     inp = W.grok()
-    rows = [0, 1, 63, 64, 127, 128, 4095, 8000, 8190, 8191]
-    pair, worst = _sampled_prefill(W.GROK, inp, None, rows, layers=2)
-    say(f"  worst row-relative error {worst:.3e}")
+    sh = W.GROK
+    pps = sh.n // 16 + 4
+    pair = Pair(2, sh.Hkv, sh.d, pps, 1, pps, sh.dtype, sh.theta)
+    O, _ = pair.prefill(0, [0], inp.Q, inp.K, inp.V, inp.mask, inp.positions, oracle=False)
+    worst = _all_rows(pair, O, inp, [0])
+    say(f"  worst row-relative error {worst:.3e} over {48 * 8192} rows")
+    pair.check_cache([0], invariants=False)
     # second layer holds 8191 tokens, then one appended token and a decode at T=8192
     K2 = W.normal((1, 8, 8191, 128), 7004)
     V2 = W.normal((1, 8, 8191, 128), 7005)
@@ -305,10 +326,15 @@ def test_grok_full_size_sampled():
     pair.append(1, [0], st.k, st.v, torch.ones((1, 1), dtype=torch.uint8), torch.tensor([[8191]], dtype=torch.int32))
     o, r = pair.decode(1, [0], st.q, [8192])
     compare_rows(o, r, torch.bfloat16)
+    pair.lib.gqa_workspace_status(pair.gpu.handle, pair.ws)
+    pair.check_cache([0])
 
 
-def test_serving_decode_full_size_sampled():
-    say("case: serving decode, 64 sequences, lengths log-uniform [512, 32768], Hq=32 Hkv=8 d=128")
+def test_serving_decode_full_size():
+    """Serving decode: 64 sequences with cached lengths log-uniform in
+    [512, 32768] (Hq=32, Hkv=8, d=128), one batched append and one decode: the
+    output of every sequence and head, every block table and every cache byte."""
+    say("case: serving decode, 64 sequences, lengths log-uniform [512, 32768], Hq=32 Hkv=8 d=128, all sequences")
     import causal_gqa_attention_attn_amd as lib
     from oracle.cache_model import CacheModel
     lens = W.serving_lengths()
@@ -335,6 +361,7 @@ def test_serving_decode_full_size_sampled():
     ws = torch.zeros(lib.gqa_workspace_size(cache.handle, B, 32), dtype=torch.uint8, device="cuda")
     lib.gqa_decode(cache.handle, 0, list(range(B)), st.q.cuda(), [x + 1 for x in lens], o, ws)
     torch.cuda.synchronize()
+    lib.gqa_workspace_status(cache.handle, ws)
     # block tables: a values-free run of the oracle's allocator with the same lengths
     alloc = CacheModel(1, 1, 2, 16, pages, B, 32768 // 16 + 2, dtype="f32", free_order=order)
     z = np.zeros((B, 1, n_max, 2), np.float32)
@@ -343,35 +370,41 @@ def test_serving_decode_full_size_sampled():
                  np.ones((B, 1), np.uint8), np.array([[x] for x in lens]))
     for b in range(B):
         assert lib.gqa_cache_page_table(cache.handle, b) == alloc.page_table(b)
-    # outputs of sampled sequences: shortest, longest and two others
-    order_by_len = sorted(range(B), key=lambda b: lens[b])
-    for b in [order_by_len[0], order_by_len[-1], 5, 40]:
+    oc = o.cpu()
+    # every sequence: its own oracle cache (rotation and bf16 rounding of its
+    # keys), the decode output and the cache bytes; sequences run on a thread pool
+    kv = [(W.normal_device((8, L, 128), 91000 + b).cpu(), W.normal_device((8, L, 128), 92000 + b).cpu(),
+           gather(cache, b, 0)) for b, L in enumerate(lens)]
+
+    def one(b):
         L = lens[b]
         ref = CacheModel(1, 8, 128, 16, -(-(L + 1) // 16), 1, -(-(L + 1) // 16), dtype="bf16",
                          rope_theta=5e5, max_position=32770)
-        kb = W.normal_device((8, L, 128), 91000 + b).cpu()
-        vb = W.normal_device((8, L, 128), 92000 + b).cpu()
+        kb, vb, (gk, gv) = kv[b]
         k = torch.cat([kb, st.k[b]], dim=1)[None]
         v = torch.cat([vb, st.v[b]], dim=1)[None]
         ref.append(0, [0], as_f32(k), as_f32(v), np.ones((1, L + 1), np.uint8), np.arange(L + 1)[None])
         r = ref.decode(0, [0], as_f32(st.q[b:b + 1]), [L + 1])
-        compare_rows(o[b:b + 1], r, torch.bfloat16)
-        gk, gv = cache.gather(b, 0)
-        assert np.array_equal(gk.float().numpy().view(np.uint32), ref.keys(0, 0).view(np.uint32))
-        assert np.array_equal(gv.float().numpy().view(np.uint32), ref.values(0, 0).view(np.uint32))
+        _, rel = compare_rows(oc[b:b + 1], r, torch.bfloat16)
+        assert np.array_equal(gk.float().numpy().view(np.uint32), ref.keys(0, 0).view(np.uint32)), f"K of {b}"
+        assert np.array_equal(gv.float().numpy().view(np.uint32), ref.values(0, 0).view(np.uint32)), f"V of {b}"
+        return rel
+
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=oracle_workers()) as ex:
+        worst = max(ex.map(one, sorted(range(B), key=lambda b: -lens[b])))
+    say(f"  worst row-relative error {worst:.3e} over {B} sequences x 32 heads")
     cache.close()
 
 
-def test_edit_full_size_sampled():
+def test_edit_full_size():
     """Prompt edit at full size, in the call the benchmark times: 16 sequences of
     4096 tokens (Hq=32 Hkv=8 d=128) prefilled, each truncated at its seeded edit
     position m_b, then the suffix re-prefilled from new rows (the deep-layer case
     of an edit).  The kept prefix [0, m_b) of every sequence must be byte-identical
-    before and after; sampled suffix rows of four sequences (the shortest and
-    longest kept prefixes among them) are compared with the oracle, and their
-    whole caches and block tables bit for bit."""
+    before and after; every suffix row of all 16 sequences is compared with the
+    oracle, and all caches and block tables bit for bit."""
     sh = W.EDIT
-    say(f"case: edit re-prefill, B={sh.B} n={sh.n} Hq={sh.Hq} Hkv={sh.Hkv} d={sh.d}, sampled rows")
+    say(f"case: edit re-prefill, B={sh.B} n={sh.n} Hq={sh.Hq} Hkv={sh.Hkv} d={sh.d}, every suffix row")
     full = W.prefill_inputs(sh, 1006)
     ms = W.edit_points(sh.B, sh.n)
     lens = [sh.n - m for m in ms]
@@ -381,27 +414,17 @@ def test_edit_full_size_sampled():
                 max_position=sh.n + 32, free_order=W.page_order(sh.B * (sh.n // 16) + 16, 1006))
     ids = list(range(sh.B))
     pair.prefill(0, ids, full.Q, full.K, full.V, full.mask, full.positions, oracle=False)
-    before = [pair.gpu.gather(b, 0) for b in ids]
+    before = [gather(pair.gpu, b, 0) for b in ids]
     for b, m in zip(ids, ms):
         pair.truncate(b, m)
     Os, _ = pair.prefill(0, ids, suffix.Q, suffix.K, suffix.V, suffix.mask, suffix.positions, oracle=False)
-    Oc = Os.cpu()
     for b, m in zip(ids, ms):
-        k, v = pair.gpu.gather(b, 0)
+        k, v = gather(pair.gpu, b, 0)
         assert torch.equal(k[:, :m].view(torch.int16), before[b][0][:, :m].view(torch.int16)), f"prefix K of {b}"
         assert torch.equal(v[:, :m].view(torch.int16), before[b][1][:, :m].view(torch.int16)), f"prefix V of {b}"
-    by_m = sorted(ids, key=lambda b: ms[b])
-    sample = [by_m[0], by_m[-1], by_m[len(by_m) // 2], 3]
-    worst = 0.0
-    for b in sample:
-        L = lens[b]
-        rows = sorted({0, 1, L // 2, L - 2, L - 1} & set(range(L)))
-        ref = pair.ref.prefill_rows(0, b, as_f32(suffix.Q[b, :, rows, :]), [ms[b] + r for r in rows])
-        _, rel = compare_rows(Oc[b, :, rows, :], ref, sh.dtype)
-        worst = max(worst, rel)
-        assert torch.all(Oc[b, :, L:, :] == 0), "padding rows of the suffix must be written as 0"
-    say(f"  worst row-relative error {worst:.3e}")
-    pair.check_cache(sample)
+    worst = _all_rows(pair, Os, suffix, ids, starts=ms)
+    say(f"  worst row-relative error {worst:.3e} over {sum(lens) * sh.Hq} suffix rows")
+    pair.check_cache(ids)
 
 
 def test_attention_half_matches_prefill():
@@ -514,8 +537,8 @@ def test_decode_step_fused(Hq, Hkv, lengths):
         assert torch.equal(o1.cpu().view(torch.int16), o2.cpu().view(torch.int16)), f"step {t}"
     a.check_cache(ids)
     for s in ids:
-        ka, va = a.gpu.gather(s, 0)
-        kb, vb = b.gpu.gather(s, 0)
+        ka, va = gather(a.gpu, s, 0)
+        kb, vb = gather(b.gpu, s, 0)
         assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
         assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
 
@@ -558,7 +581,7 @@ def _poison_stale(pair, seq, layers):
     """NaN into every slot of the sequence's pages at or past its length."""
     lib = pair.lib
     pages = lib.gqa_cache_page_table(pair.gpu.handle, seq)
-    kv, vv = pair.gpu.k_view(), pair.gpu.v_view()
+    kv, vv = k_view(pair.gpu), v_view(pair.gpu)
     for l in layers:
         n = lib.gqa_cache_length(pair.gpu.handle, seq, l)
         for lp, ph in enumerate(pages):

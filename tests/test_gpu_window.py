@@ -77,6 +77,53 @@ def test_window_prefill_and_decode(dtype, Hq, Hkv, d, win):
     pair.check_cache(ids)
 
 
+@pytest.mark.parametrize("win", [1, 5, 100])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (24, 8)])
+def test_window_odd_group_sizes(Hq, Hkv, win):
+    """Odd Hq/Hkv (MHA, three heads per group) takes 128-token query tiles, whose
+    last rows can start their windows two key tiles after the first row's.  A
+    256-token chunk at position 0, then one of 200 at 256 and one of 130 at 456:
+    the second query tile of each chunk has rows whose window lies wholly in the
+    third key tile its workgroup reads."""
+    say(f"case: window {win}, odd group Hq={Hq} Hkv={Hkv}, 128-token query tiles")
+    d = 128
+    chunks = [256, 200, 130]
+    R = _ring_pages(win, max(chunks)) + 1
+    pair = Pair(1, Hkv, d, R + 4, 1, R, torch.bfloat16, 1e4, max_position=1024,
+                free_order=W.page_order(R + 4, 43), window=win)
+    pair.gpu.k_pool.fill_(float("nan"))
+    pair.gpu.v_pool.fill_(float("nan"))
+    c = 0
+    for i, n in enumerate(chunks):
+        shape = W.AttnShape(B=1, n=n, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4)
+        _chunk(pair, 0, [0], shape, 560 + i, [n], [c])
+        c += n
+    pair.check_cache([0])
+
+
+@pytest.mark.parametrize("win", [1, 5, 100])
+def test_window_odd_group_large_negative_logits(win):
+    """Every score of every row far below zero (q close to -4u, k close to 4u for
+    a fixed u, no rotation: logits near -180): the softmax must still be exact
+    for rows whose window starts two key tiles after their workgroup's first
+    row, where a reference that misses the row's keys would underflow every
+    probability."""
+    say(f"case: window {win}, Hq=Hkv=8, all logits near -180")
+    Hq = Hkv = 8
+    d, n = 128, 256
+    R = _ring_pages(win, n) + 1
+    pair = Pair(1, Hkv, d, R + 4, 1, R, torch.bfloat16, 0.0, max_position=1024, window=win)
+    u = W.normal((1, 1, 1, d), 580, torch.float32)
+    Q = (-4.0 * u + 0.1 * W.normal((1, Hq, n, d), 581, torch.float32)).to(torch.bfloat16)
+    K = (4.0 * u + 0.1 * W.normal((1, Hkv, n, d), 582, torch.float32)).to(torch.bfloat16)
+    V = W.normal((1, Hkv, n, d), 583, torch.bfloat16)
+    mask = torch.ones((1, n), dtype=torch.uint8)
+    pos = torch.arange(n, dtype=torch.int32)[None]
+    O, ref = pair.prefill(0, [0], Q, K, V, mask, pos)
+    compare_rows(O, ref, torch.bfloat16)
+    pair.check_cache([0])
+
+
 def test_window_long_ring_many_wraps():
     """One sequence, W = 512 on a 50-page ring: 4096 prompt tokens in chunks of
     256, then 64 decode steps, the ring wrapping five times."""
