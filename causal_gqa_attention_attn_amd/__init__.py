@@ -31,7 +31,8 @@ F32, BF16 = 0, 1
 STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "MASK", -5: "POSITION",
           -6: "CACHE", -7: "OUT_OF_PAGES", -8: "UNSUPPORTED", -9: "HIP", -10: "DEVICE"}
 EXPORTS = ["gqa_cache_buffer_sizes", "gqa_cache_create", "gqa_cache_destroy", "kv_cache_append",
-           "gqa_prefill", "gqa_attention", "gqa_decode", "gqa_decode_step", "kv_cache_truncate", "kv_cache_fork", "kv_cache_remap", "gqa_cache_length",
+           "gqa_prefill", "gqa_attention", "gqa_decode", "gqa_decode_step", "gqa_decode_step_noalloc",
+           "kv_cache_truncate", "kv_cache_fork", "kv_cache_remap", "gqa_cache_length",
            "gqa_cache_page_table", "gqa_cache_free_pages", "gqa_cache_check", "gqa_workspace_size",
            "gqa_attention_workspace_size", "gqa_workspace_status", "gqa_set_merge_wait",
            "gqa_prefix_index_create", "gqa_prefix_index_destroy",
@@ -75,6 +76,7 @@ _sig = {
     "gqa_attention": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _P, _P, _TP, _P, ctypes.c_size_t, _P],
     "gqa_decode": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _P, _TP, _P, ctypes.c_size_t, _P],
     "gqa_decode_step": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _TP, _TP, _TP, _P, ctypes.c_size_t, _P],
+    "gqa_decode_step_noalloc": [_P, ctypes.c_int32, ctypes.c_int32, _P, _TP, _TP, _TP, _TP, _P],
     "kv_cache_truncate": [_P, ctypes.c_int32, ctypes.c_int32],
     "kv_cache_fork": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
     "gqa_prefix_index_create": [_P],
@@ -227,6 +229,14 @@ def gqa_decode_step(handle, layer, seq_ids, q, k_new, v_new, o, workspace=None, 
                                 ctypes.byref(tv), ctypes.byref(to), ws, nbytes, _stream(stream)), "gqa_decode_step")
 
 
+def gqa_decode_step_noalloc(handle, layer, seq_ids, q, k_new, v_new, o, stream=None):
+    ids = _host_i32(seq_ids)
+    tq, tk, tv, to = _tensor(q), _tensor(k_new), _tensor(v_new), _tensor(o)
+    _check(_lib.gqa_decode_step_noalloc(handle, layer, len(ids), _ptr(ids), ctypes.byref(tq), ctypes.byref(tk),
+                                        ctypes.byref(tv), ctypes.byref(to), _stream(stream)),
+           "gqa_decode_step_noalloc")
+
+
 def kv_cache_truncate(handle, seq_id, m):
     _check(_lib.kv_cache_truncate(handle, seq_id, m), "kv_cache_truncate")
 
@@ -305,9 +315,11 @@ def gqa_attention_workspace_size(handle, B, Hq, n) -> int:
 
 def gqa_workspace_status(handle, workspace, clear=False, stream=None):
     """Raises GqaError (GQA_ERR_DEVICE) if a split combine using this workspace
-    gave up since the status was last cleared; clear=True resets it after the read."""
-    nbytes = workspace.numel() * workspace.element_size()
-    _check(_lib.gqa_workspace_status(handle, workspace.data_ptr(), nbytes, 1 if clear else 0, _stream(stream)),
+    gave up since the status was last cleared; clear=True resets it after the
+    read.  workspace None: the static scratch of gqa_decode_step_noalloc."""
+    ptr = None if workspace is None else workspace.data_ptr()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.gqa_workspace_status(handle, ptr, nbytes, 1 if clear else 0, _stream(stream)),
            "gqa_workspace_status")
 
 

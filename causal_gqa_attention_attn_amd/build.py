@@ -16,7 +16,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgqa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "prefix_index.cpp", "cache_ops.hip", "attend_f32.hip", "prefill_bf16.hip", "decode_bf16.hip"]
+SOURCES = ["api.cpp", "prefix_index.cpp", "cache_ops.hip", "attend_f32.hip", "prefill_bf16.hip", "decode_bf16.hip",
+           "scratch.hip"]
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -712,15 +712,26 @@ struct WsView {
 
 int64_t ws_slot_bytes(int64_t d) { return (16 * d + 16 * 2 + gqa::kDecodeMergers) * 4; }
 
-WsView ws_view(void* ws, size_t bytes, int64_t d) {
-  WsView v;
-  if (!ws || bytes < static_cast<size_t>(2 * kWsHeader)) return v;
+// count_d: head dimension the slot count is taken for (d itself for a caller's
+// workspace; the largest, 128, for the static scratch, whose flags must sit at
+// the same place for caches of any d)
+int64_t ws_slots(size_t bytes, int64_t count_d) {
   // the header and the 256-byte rounding of the flags fit in 2 * kWsHeader
-  v.slots = static_cast<int64_t>((bytes - 2 * kWsHeader) / ws_slot_bytes(d));
+  return bytes < static_cast<size_t>(2 * kWsHeader)
+             ? 0 : static_cast<int64_t>((bytes - 2 * kWsHeader) / ws_slot_bytes(count_d));
+}
+
+// bytes of the header and the ready flags of `slots` slots
+int64_t ws_zero_bytes(int64_t slots) { return kWsHeader + ceil_div(slots * gqa::kDecodeMergers * 4, 256) * 256; }
+
+WsView ws_view(void* ws, size_t bytes, int64_t d, int64_t count_d = 0) {
+  WsView v;
+  if (!ws) return v;
+  v.slots = ws_slots(bytes, count_d ? count_d : d);
+  if (!v.slots) return v;
   v.status = static_cast<int32_t*>(ws);
   v.flags = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kWsHeader);
-  const int64_t flag_bytes = ceil_div(v.slots * gqa::kDecodeMergers * 4, 256) * 256;
-  v.zero_bytes = kWsHeader + flag_bytes;
+  v.zero_bytes = ws_zero_bytes(v.slots);
   v.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + v.zero_bytes);
   v.part_h = v.part_o + v.slots * 16 * d;
   return v;
@@ -783,7 +794,7 @@ size_t ws_bytes_for(const gqa_cache* c, int64_t B, int64_t ys) {
 gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
                         const gqa_tensor* o, const int32_t* start, const int32_t* count, const int32_t* row0,
                         int n_rect, int ncol, const gqa_tensor* k_new, const gqa_tensor* v_new, void* workspace,
-                        size_t ws_bytes, hipStream_t s) {
+                        size_t ws_bytes, hipStream_t s, int64_t count_d = 0) {
   const gqa_cache_config& cf = c->cfg;
   const int64_t Hq = q->shape[1];
   const int64_t ys = split_ys(c, ncol);
@@ -793,7 +804,7 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
     Tr[b] = read_length(c, start[b], count[b]);
   }
   const int pps = decode_pages_per_split(Tr.data(), B, ys);
-  const WsView wv = ws_view(workspace, ws_bytes, cf.head_dim);
+  const WsView wv = ws_view(workspace, ws_bytes, cf.head_dim, count_d);
   gqa_status st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
   int64_t split_base = 0;
@@ -858,12 +869,12 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
 
 gqa_status launch_decode(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
                          const gqa_tensor* o, const int32_t* T, const gqa_tensor* k_new, const gqa_tensor* v_new,
-                         void* workspace, size_t ws_bytes, hipStream_t s) {
+                         void* workspace, size_t ws_bytes, hipStream_t s, int64_t count_d = 0) {
   std::vector<int32_t> start(B), count(B, 1), row0(B, 0);
   for (int b = 0; b < B; ++b) start[b] = T[b] - 1;
   const int G = static_cast<int>(q->shape[1] / c->cfg.num_kv_heads);
   return launch_split(c, layer, B, seq_ids, q, o, start.data(), count.data(), row0.data(), 1, G, k_new, v_new,
-                      workspace, ws_bytes, s);
+                      workspace, ws_bytes, s, count_d);
 }
 
 gqa_status launch_decode_f32(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
@@ -938,6 +949,17 @@ gqa_status check_workspace(const gqa_cache* c, int32_t B, int64_t ncol, const in
   return GQA_OK;
 }
 
+// Workspace slots a split-T call over lengths T takes (0 when every sequence
+// fits one split and no workspace is needed).
+int64_t split_slots_needed(const gqa_cache* c, int32_t B, int64_t ncol, const int32_t* T) {
+  if (c->cfg.dtype != GQA_BF16 || B == 0) return 0;
+  const int64_t ys = split_ys(c, ncol);
+  const int pps = decode_pages_per_split(T, B, ys);
+  int64_t total_splits = 0;
+  for (int b = 0; b < B; ++b) total_splits += split_count(T[b], pps);
+  return total_splits <= B ? 0 : total_splits * ys;
+}
+
 // Lengths a split-T call reads: start + count keys; a sequence with no query
 // reads none (its single split only zeroes its rows of O).  The split path
 // takes one entry per batch row, in batch order.
@@ -1002,10 +1024,18 @@ GQA_EXPORT size_t gqa_attention_workspace_size(const gqa_cache* c, int32_t B, in
 GQA_EXPORT gqa_status gqa_workspace_status(const gqa_cache* c, void* workspace, size_t ws_bytes, int32_t clear,
                                            void* stream) {
   if (!c) return fail(GQA_ERR_ARG, "cache is null");
-  const WsView wv = ws_view(workspace, ws_bytes, c->cfg.head_dim);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t count_d = 0;
+  if (!workspace && ws_bytes == 0) {
+    // the static scratch of the current device (set up here if no call has)
+    hipError_t e = gqa::static_scratch(ws_zero_bytes(ws_slots(gqa::kStaticScratchBytes, 128)), s, &workspace);
+    if (e != hipSuccess) return hip_fail(e, "static scratch set-up");
+    ws_bytes = static_cast<size_t>(gqa::kStaticScratchBytes);
+    count_d = 128;
+  }
+  const WsView wv = ws_view(workspace, ws_bytes, c->cfg.head_dim, count_d);
   if (!wv.slots) return fail(GQA_ERR_ARG, "workspace missing or smaller than one slot");
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GQA_ERR_ARG, "workspace must be 256-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t word = 0;
   hipError_t e = hipMemcpyAsync(&word, wv.status, sizeof(word), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -1054,9 +1084,13 @@ GQA_EXPORT gqa_status gqa_decode(gqa_cache* c, int32_t layer, int32_t B, const i
   return launch_decode(c, layer, B, seq_ids, q, o, valid_lengths, nullptr, nullptr, workspace, ws_bytes, s);
 }
 
-GQA_EXPORT gqa_status gqa_decode_step(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
-                                      const gqa_tensor* q, const gqa_tensor* k_new, const gqa_tensor* v_new,
-                                      const gqa_tensor* o, void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+// gqa_decode_step on a caller's workspace, or (static_scratch) on the
+// library's static scratch of the current device, which allocates nothing.
+gqa_status decode_step(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids, const gqa_tensor* q,
+                       const gqa_tensor* k_new, const gqa_tensor* v_new, const gqa_tensor* o, void* workspace,
+                       size_t ws_bytes, void* stream, bool static_scratch) {
   if (!c) return fail(GQA_ERR_ARG, "cache is null");
   const gqa_cache_config& cf = c->cfg;
   if (layer < 0 || layer >= cf.num_layers) return fail(GQA_ERR_ARG, "layer out of range");
@@ -1075,12 +1109,32 @@ GQA_EXPORT gqa_status gqa_decode_step(gqa_cache* c, int32_t layer, int32_t B, co
   if (plan.n != 1) return fail(GQA_ERR_SHAPE, "k_new and v_new must hold one token: [B, Hkv, 1, d]");
   std::vector<int32_t> T(B);
   for (int b = 0; b < B; ++b) T[b] = pos[b] + 1;
-  st = check_workspace(c, B, q->shape[1] / cf.num_kv_heads, decode_read_lengths(c, B, T.data()).data(),
-                       workspace, ws_bytes,
-                       gqa_workspace_size(c, B, static_cast<int32_t>(q->shape[1])));
-  if (st != GQA_OK) return st;
-  commit_append(c, layer, B, seq_ids, plan);
+  const int64_t ncol = q->shape[1] / cf.num_kv_heads;
+  const std::vector<int32_t> Tr = decode_read_lengths(c, B, T.data());
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (static_scratch) {
+    const int64_t need = split_slots_needed(c, B, ncol, Tr.data());
+    void* base = nullptr;
+    if (need > 0) {
+      const int64_t have = ws_slots(gqa::kStaticScratchBytes, 128);
+      if (need > have)
+        return fail(GQA_ERR_UNSUPPORTED, "the call needs " + std::to_string(need) + " split slots (" +
+                                             std::to_string(2 * kWsHeader + need * ws_slot_bytes(128)) +
+                                             " bytes), more than the static scratch holds (" +
+                                             std::to_string(have) + " slots, " +
+                                             std::to_string(gqa::kStaticScratchBytes) +
+                                             " bytes): use gqa_decode_step with a workspace");
+      hipError_t e = gqa::static_scratch(ws_zero_bytes(have), s, &base);
+      if (e != hipSuccess) return hip_fail(e, "static scratch set-up");
+    }
+    workspace = base;
+    ws_bytes = base ? static_cast<size_t>(gqa::kStaticScratchBytes) : 0;
+  } else {
+    st = check_workspace(c, B, ncol, Tr.data(), workspace, ws_bytes,
+                         gqa_workspace_size(c, B, static_cast<int32_t>(q->shape[1])));
+    if (st != GQA_OK) return st;
+  }
+  commit_append(c, layer, B, seq_ids, plan);
   if (cf.dtype != GQA_BF16) {
     st = sync_metadata(c, s);
     if (st != GQA_OK) return st;
@@ -1088,7 +1142,22 @@ GQA_EXPORT gqa_status gqa_decode_step(gqa_cache* c, int32_t layer, int32_t B, co
     if (st != GQA_OK) return st;
     return launch_decode_f32(c, layer, B, seq_ids, q, o, T.data(), s);
   }
-  return launch_decode(c, layer, B, seq_ids, q, o, T.data(), k_new, v_new, workspace, ws_bytes, s);
+  return launch_decode(c, layer, B, seq_ids, q, o, T.data(), k_new, v_new, workspace, ws_bytes, s,
+                       static_scratch ? 128 : 0);
+}
+
+}  // namespace
+
+GQA_EXPORT gqa_status gqa_decode_step(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
+                                      const gqa_tensor* q, const gqa_tensor* k_new, const gqa_tensor* v_new,
+                                      const gqa_tensor* o, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_step(c, layer, B, seq_ids, q, k_new, v_new, o, workspace, ws_bytes, stream, false);
+}
+
+GQA_EXPORT gqa_status gqa_decode_step_noalloc(gqa_cache* c, int32_t layer, int32_t B, const int32_t* seq_ids,
+                                              const gqa_tensor* q, const gqa_tensor* k_new,
+                                              const gqa_tensor* v_new, const gqa_tensor* o, void* stream) {
+  return decode_step(c, layer, B, seq_ids, q, k_new, v_new, o, nullptr, 0, stream, true);
 }
 
 // ------------------------------------------------------------------ truncate / remap

@@ -14,6 +14,7 @@ constexpr int kMaxRowsPerLaunch = 64;    // batch rows of one attention launch (
 constexpr int kMaxPatchPerLaunch = 496;   // block-table entries (or page copies) per launch; the arguments stay under 4 KiB
 constexpr int kMaxSplitDecode = 128;   // splits per sequence in one decode launch
 constexpr int kDecodeMergers = 4;      // splits of a sequence that combine the split records
+constexpr int64_t kStaticScratchBytes = int64_t{48} << 20;   // the library's static split-T scratch per device
 
 // Per-entry metadata of one launch (an entry is one run of valid tokens of a
 // sequence, or a whole decode row).
@@ -154,5 +155,8 @@ hipError_t launch_attend_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t s);
 hipError_t launch_page_copy(const CopyArgs& a, int num_layers, hipStream_t s);
+// Device address of the static split-T scratch on the current device; the
+// first call on a device resolves it and zero-fills its first zero_bytes on s.
+hipError_t static_scratch(int64_t zero_bytes, hipStream_t s, void** out);
 
 }  // namespace gqa

@@ -230,6 +230,25 @@ gqa_status gqa_decode_step(gqa_cache* cache, int32_t layer, int32_t B, const int
                            const gqa_tensor* q, const gqa_tensor* k_new, const gqa_tensor* v_new,
                            const gqa_tensor* o, void* workspace, size_t ws_bytes, void* stream);
 
+/* gqa_decode_step without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results, cache contents and page
+ * assignment as gqa_decode_step; the split partials, ready flags and status
+ * word live in the library's static scratch instead: a 48 MiB device array
+ * that each GPU the library runs on holds until the process ends, set up on
+ * the first call on each device (with that device current) and reused by
+ * every later call there.  No device memory is allocated and no memset is
+ * recorded (the first call zero-fills the flags with a kernel on `stream`).
+ * Calls on one device share the scratch: calls that overlap in time (two
+ * streams, two threads) race and must be ordered by the caller.  A call whose
+ * split records would not fit (GQA_ERR_UNSUPPORTED, nothing changed) needs
+ * gqa_decode_step with a workspace; at Hkv = 8 and d = 128 every call of up to
+ * 64 sequences fits.  gqa_workspace_status(cache, NULL, 0, ...) reads and
+ * clears the scratch's status word on the current device. */
+gqa_status gqa_decode_step_noalloc(gqa_cache* cache, int32_t layer, int32_t B, const int32_t* seq_ids,
+                                   const gqa_tensor* q, const gqa_tensor* k_new, const gqa_tensor* v_new,
+                                   const gqa_tensor* o, void* stream);
+
 /* Prompt edit at position m ([P3] prompt-edit lesson): keep positions [0,m) in
  * every layer of seq_id, drop the rest and give up the sequence's references to
  * the pages no layer still uses; a page whose last reference goes returns to
@@ -329,8 +348,10 @@ size_t gqa_attention_workspace_size(const gqa_cache* cache, int32_t B, int32_t H
  * GQA_ERR_DEVICE if one has.  With clear != 0 the word and every ready flag
  * are zeroed afterwards (on `stream`, waited for), which makes the workspace
  * as good as freshly zero-filled: do this after GQA_ERR_DEVICE before reusing
- * it.  GQA_ERR_ARG for a null cache or a workspace too small for one slot;
- * GQA_ERR_HIP if the read fails.  Synchronises: not for use under capture. */
+ * it.  workspace NULL with ws_bytes 0 means the static scratch of
+ * gqa_decode_step_noalloc on the current device.  GQA_ERR_ARG for a null
+ * cache or a workspace too small for one slot; GQA_ERR_HIP if the read fails.
+ * Synchronises: not for use under capture. */
 gqa_status gqa_workspace_status(const gqa_cache* cache, void* workspace, size_t ws_bytes, int32_t clear,
                                 void* stream);
 
