@@ -75,42 +75,154 @@ def _traffic(kernel_key, source):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _blas_threads():
+def _profiled_us(kernel_key, source):
+    """Average duration (us) of a kernel in the committed rocprofv3 kernel trace
+    of the same workload, if it was taken on the kernel source built now."""
+    path = os.path.join(ROOT, "profiles", "kernels.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_sha256") != _sha(source):
+        return None
+    return rec.get("avg_us")
+
+
+def _blas_info():
+    """(threads, description) of the BLAS numpy calls into."""
     try:
         from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
-        return max(n) if n else 1
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return (int(i.get("num_threads") or 1),
+                        f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')}, "
+                        f"{os.path.basename(i.get('filepath', ''))})")
     except Exception:
-        return os.cpu_count() or 1
+        pass
+    return os.cpu_count() or 1, "unknown"
 
 
-def cpu_baseline(inp, budget_s):
-    """Float64 oracle on a bounded sample: blocks of 64 query rows spread over
-    the sequence (all 48 heads), until ``budget_s`` seconds of work; reported as
-    causal TFLOP/s over the rows done (4*d*(p+1) flops per row and head)."""
+def _host():
+    """CPU model, physical cores and logical CPUs of this host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        import psutil
+        phys = psutil.cpu_count(logical=False)
+    except Exception:
+        phys = None
+    return {"cpu_model": model, "physical_cores": phys, "logical_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def _oracle_prefill_rate(m, Q, n, Hq, budget_s, block=64):
+    """Causal TFLOP/s of the oracle's prefill rows of one sequence (cache m,
+    layer 0): blocks of ``block`` query rows interleaved so that any prefix of
+    the list is spread over the sequence, heaviest first within each sweep,
+    until ``budget_s`` seconds of work.  4*d*(p+1) flops per row and head."""
+    stride = 16 * block
+    blocks = [r0 for off in range(stride // block) for r0 in range(n - block - block * off, -1, -stride)]
+    rows_done, flops, t_used = 0, 0.0, 0.0
+    for r0 in blocks:
+        rows = list(range(r0, r0 + block))
+        t = time.perf_counter()
+        m.prefill_rows(0, 0, Q[:, r0:r0 + block], rows)
+        t_used += time.perf_counter() - t
+        rows_done += block
+        flops += sum(4.0 * D * (p + 1) for p in rows) * Hq
+        if t_used >= budget_s:
+            break
+    return flops / t_used / 1e12, rows_done, t_used
+
+
+def cpu_baseline(inp, budget_s, W):
+    """The float64 oracle as it stands, on bounded samples of the benchmark's
+    workloads, on this host's cores:
+      * value: the Grok-shaped prefill, blocks of 64 query rows spread over the
+        sequence (all 48 heads), until ``budget_s`` seconds of work, with numpy's
+        BLAS on all its threads; causal TFLOP/s of the rows done;
+      * llama_prefill_1thread: the same measurement on the Llama-shaped
+        prefill (one sequence of the B=8 batch) with BLAS held to one thread;
+      * decode_step: one oracle decode step (append of the new token and one
+        query over the cache) of the Grok-shaped 64-layer decode at T=8192 and
+        of the 64-sequence serving decode, timed on a few layers or sequences
+        and scaled to the whole step by the keys read."""
     import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
     from oracle.cache_model import CacheModel
+    threads, blas = _blas_info()
     K = inp.K.float().numpy()
     V = inp.V.float().numpy()
     Q = inp.Q.float().numpy()
     m = CacheModel(1, HKV, D, 16, N // 16, 1, N // 16, dtype="bf16", rope_theta=THETA, max_position=N)
     m.append(0, [0], K, V, np.ones((1, N), np.uint8), np.arange(N)[None])
-    # all 64-row blocks, interleaved so that any prefix of the list is spread over
-    # the sequence (heaviest first within each sweep)
-    blocks = [r0 for off in range(16) for r0 in range(N - 64 - 64 * off, -1, -1024)]
-    rows_done, flops, t_used = 0, 0.0, 0.0
-    for r0 in blocks:
-        rows = list(range(r0, r0 + 64))
+    rate, rows_done, t_used = _oracle_prefill_rate(m, Q[0], N, HQ, budget_s)
+    out = {"value": rate, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{rows_done} query rows x {HQ} heads of the n=8192 prefill (blocks of 64 rows "
+                     f"spread over the sequence, heaviest first), float64 numpy, {t_used:.1f} s",
+           "blas": blas, "blas_threads": threads, **_host()}
+    # Llama-shaped prefill on one BLAS thread
+    sh = W.LLAMA
+    li = W.llama()
+    lm = CacheModel(1, sh.Hkv, sh.d, 16, sh.n // 16, 1, sh.n // 16, dtype="bf16", rope_theta=sh.theta,
+                    max_position=sh.n)
+    lm.append(0, [0], li.K[:1].float().numpy(), li.V[:1].float().numpy(), np.ones((1, sh.n), np.uint8),
+              np.arange(sh.n)[None])
+    with threadpool_limits(1):
+        lrate, lrows, lt = _oracle_prefill_rate(lm, li.Q[0].float().numpy(), sh.n, sh.Hq, budget_s / 3)
+    out["llama_prefill_1thread"] = {"value": lrate, "unit": "TFLOP/s", "threads": 1,
+                                    "sample": f"{lrows} query rows x {sh.Hq} heads of one n=2048 sequence, "
+                                              f"{lt:.1f} s"}
+    # decode steps: Grok-shaped (64 layers of 8192 keys), timed on 2 layers
+    def step_seconds(model, seq, T, q, k, v, reps=3):
         t = time.perf_counter()
-        m.prefill_rows(0, 0, Q[0, :, r0:r0 + 64], rows)
-        t_used += time.perf_counter() - t
-        rows_done += 64
-        flops += sum(4.0 * D * (p + 1) for p in rows) * HQ
-        if t_used >= budget_s:
-            break
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
-            "sample": f"{rows_done} query rows x {HQ} heads of the n=8192 prefill (blocks of 64 rows "
-                      f"spread over the sequence, heaviest first), float64 numpy, {t_used:.1f} s"}
+        for _ in range(reps):
+            model.truncate(seq, T - 1)
+            model.append(0, [seq], k, v, np.ones((1, 1), np.uint8), np.array([[T - 1]]))
+            model.decode(0, [seq], q, [T])
+        return (time.perf_counter() - t) / reps
+    g_layers, g_t = 2, 0.0
+    for l in range(g_layers):
+        kf = W.normal((1, HKV, N - 1, D), 70000 + l).float().numpy()
+        vf = W.normal((1, HKV, N - 1, D), 80000 + l).float().numpy()
+        gm = CacheModel(1, HKV, D, 16, N // 16, 1, N // 16, dtype="bf16", rope_theta=THETA, max_position=N + 16)
+        gm.append(0, [0], kf, vf, np.ones((1, N - 1), np.uint8), np.arange(N - 1)[None])
+        st = W.decode_step_inputs(W.GROK, 1004, l)
+        g_t += step_seconds(gm, 0, N, st.q.float().numpy(), st.k.float().numpy(), st.v.float().numpy())
+    grok_step = g_t / g_layers * LAYERS
+    # serving decode: four sequences near the median length, scaled by keys read
+    lens = W.serving_lengths()
+    sv = W.SERVING
+    order = sorted(range(len(lens)), key=lambda b: abs(lens[b] - sorted(lens)[len(lens) // 2]))[:4]
+    s_t, s_keys = 0.0, 0
+    st = W.decode_step_inputs(sv, 1005, 0)
+    for b in order:
+        L = lens[b]
+        sm = CacheModel(1, sv.Hkv, sv.d, 16, L // 16 + 2, 1, L // 16 + 2, dtype="bf16", rope_theta=sv.theta,
+                        max_position=32770)
+        kb = torch.randn((1, sv.Hkv, L, sv.d), generator=torch.Generator().manual_seed(b)).numpy()
+        sm.append(0, [0], kb, kb, np.ones((1, L), np.uint8), np.arange(L)[None])
+        s_t += step_seconds(sm, 0, L + 1, st.q[b:b + 1].float().numpy(), st.k[b:b + 1].float().numpy(),
+                            st.v[b:b + 1].float().numpy())
+        s_keys += L + 1
+    serving_step = s_t * sum(x + 1 for x in lens) / s_keys
+    out["decode_step"] = {
+        "grok_64_layers_s": grok_step,
+        "grok_gbs": 2.0 * LAYERS * HKV * N * D * 2 / grok_step / 1e9,
+        "serving_64_sequences_s": serving_step,
+        "serving_gbs": sum((x + 1) * 2 * sv.Hkv * sv.d * 2 for x in lens) / serving_step / 1e9,
+        "sample": f"oracle decode step (append + decode) timed on {g_layers} of the 64 Grok-shaped layers and "
+                  f"on 4 serving sequences near the median length ({sum(lens[b] for b in order)} cached "
+                  f"tokens), scaled by keys read; GB/s counts the bf16 K/V bytes the GPU reads"}
+    return out
 
 
 def _median_ms(fn, before=None, iters=20, warm=3, reps=5):
@@ -140,11 +252,36 @@ def _median_ms(fn, before=None, iters=20, warm=3, reps=5):
     return ts[len(ts) // 2], ts[0]
 
 
-def other_configs(lib, W):
+OTHER = ["llama_prefill", "serving_decode", "verify_chunks", "shared_prompt_decode", "holey_mask_prefill",
+         "window_prefill", "window_decode", "edit_reprefill"]
+
+
+def other_configs(lib, W, only=None):
+    """The other measured configurations; ``only`` names one of OTHER to run it
+    alone (a profiling aid)."""
     import numpy as np
     import torch
     res = {}
-    # Llama-shaped prefill
+    want = lambda name: only is None or only == name
+    serving_cache = only is None or only in ("serving_decode", "verify_chunks", "window_decode",
+                                             "shared_prompt_decode")
+    if want("llama_prefill"):
+        _llama(lib, W, res)
+    if serving_cache:
+        _serving(lib, W, res, want)
+    if want("holey_mask_prefill"):
+        _holey(lib, W, res)
+    if want("window_prefill"):
+        _window_prefill(lib, W, res)
+    if want("window_decode"):
+        _window_decode(lib, W, res)
+    if want("edit_reprefill"):
+        _edit(lib, W, res)
+    return res
+
+
+def _llama(lib, W, res):
+    import torch
     inp = W.llama()
     Q, K, V = inp.Q.cuda(), inp.K.cuda(), inp.V.cuda()
     O = torch.empty_like(Q)
@@ -160,7 +297,10 @@ def other_configs(lib, W):
                             "frac": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                             "ms_median": round(med, 4), "ms_min": round(mn, 4)}
     pre.close()
-    del Q, K, V, O
+
+
+def _serving(lib, W, res, want):
+    import torch
     # serving decode
     lens = W.serving_lengths()
     Bs = len(lens)
@@ -180,17 +320,19 @@ def other_configs(lib, W):
                          lib.gqa_attention_workspace_size(cache.handle, Bs, sh.Hq, 8)), dtype=torch.uint8,
                      device="cuda")
     ids = list(range(Bs))
-    med, mn = _median_ms(lambda: lib.gqa_decode_step(cache.handle, 0, ids, q, k, v, o, ws),
-                         before=lambda: [lib.kv_cache_truncate(cache.handle, b, lens[b]) for b in ids])
-    nbytes = sum((L + 1) * 2 * sh.Hkv * sh.d * 2 for L in lens)
-    gbs = nbytes / (med * 1e-3) / 1e9
-    res["serving_decode"] = {"workload": "gqa_decode_step of 64 sequences, lengths log-uniform [512, 32768], "
-                                         "Hq=32 Hkv=8 d=128, one layer",
-                             "kv_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
-                             "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1)}
+    if want("serving_decode"):
+        med, mn = _median_ms(lambda: lib.gqa_decode_step(cache.handle, 0, ids, q, k, v, o, ws),
+                             before=lambda: [lib.kv_cache_truncate(cache.handle, b, lens[b]) for b in ids])
+        lib.gqa_workspace_status(cache.handle, ws)
+        nbytes = sum((L + 1) * 2 * sh.Hkv * sh.d * 2 for L in lens)
+        gbs = nbytes / (med * 1e-3) / 1e9
+        res["serving_decode"] = {"workload": "gqa_decode_step of 64 sequences, lengths log-uniform [512, 32768], "
+                                             "Hq=32 Hkv=8 d=128, one layer",
+                                 "kv_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                 "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1)}
     # speculative verify: a chunk of n draft tokens per sequence on the same caches,
     # split-T kernel (with workspace) beside the tiled prefill kernel (without)
-    for n in (4, 8):
+    for n in ((4, 8) if want("verify_chunks") else ()):
         chunk = W.prefill_inputs(W.AttnShape(B=Bs, n=n, Hq=sh.Hq, Hkv=sh.Hkv, d=sh.d, dtype=sh.dtype,
                                              theta=sh.theta), 1007 + n, start=lens)
         Qc, Kc, Vc = chunk.Q.cuda(), chunk.K.cuda(), chunk.V.cuda()
@@ -208,8 +350,11 @@ def other_configs(lib, W):
             "kv_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
             "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1),
             "tiled_kernel_us_median": round(tmed * 1e3, 1)}
+    lib.gqa_workspace_status(cache.handle, ws)
     trunc = None
     cache.close()
+    if not want("shared_prompt_decode"):
+        return
     # shared system prompt: 64 requests forked from one 8192-token prompt, each
     # with 512 tokens of its own, decoding together; the prompt's pages are
     # stored once and read by every request
@@ -240,6 +385,11 @@ def other_configs(lib, W):
         "note": "the prompt's 32 MiB of pages are read by all 64 requests; after the first the reads "
                 "come from L2 and the 256 MB last-level cache, so the logical rate is not an HBM rate"}
     sc.close()
+
+
+def _holey(lib, W, res):
+    import numpy as np
+    import torch
     # masks with holes: 8 rows of 2048 rectangular slots, 1536 valid tokens each in
     # 16 runs separated by padding, beside the same tokens right-padded
     sh = W.LLAMA
@@ -278,11 +428,15 @@ def other_configs(lib, W):
         "tflops": round(flops / (med * 1e-3) / 1e12, 1), "ms_median": round(med, 4), "ms_min": round(mn, 4),
         "right_padded_ms_median": round(rmed, 4)}
     pre.close()
-    del Qh, Kh, Vh, Oh
-    # sliding window W = 4096: the Grok-shaped prefill (one call, the ring holds the
-    # whole prompt) and one decode step of the 64 serving sequences (rings of
-    # 4096 + 2048 tokens, filled in 2048-token chunks)
-    WIN = 4096
+
+
+WIN = 4096
+
+
+def _window_prefill(lib, W, res):
+    import torch
+    # sliding window W = 4096: the Grok-shaped prefill (one call, the ring holds
+    # the whole prompt)
     sh = W.GROK
     inp = W.grok()
     Qg, Kg, Vg = inp.Q.cuda(), inp.K.cuda(), inp.V.cuda()
@@ -299,8 +453,17 @@ def other_configs(lib, W):
         "frac": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "ms_median": round(med, 4), "ms_min": round(mn, 4)}
     wc.close()
-    del Qg, Kg, Vg, Og
+
+
+def _window_decode(lib, W, res):
+    import torch
+    # one decode step of the 64 serving sequences over rings of 4096 + 2048
+    # tokens, filled in 2048-token chunks
     sh = W.SERVING
+    Bs = 64
+    st = W.decode_step_inputs(sh, 1005, 0)
+    q = st.q.cuda()
+    o = torch.empty_like(q)
     R = WIN // 16 + 1 + 2048 // 16
     lens = W.serving_lengths()
     pages = sum(min(R, -(-(x + 1) // 16)) for x in lens) + 8
@@ -325,7 +488,12 @@ def other_configs(lib, W):
                     "ring caches, Hq=32 Hkv=8 d=128, one layer",
         "kv_bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
         "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1)}
+    lib.gqa_workspace_status(wc.handle, wws)
     wc.close()
+
+
+def _edit(lib, W, res):
+    import torch
     # edit re-prefill
     sh = W.EDIT
     full = W.prefill_inputs(sh, 1006)
@@ -349,7 +517,6 @@ def other_configs(lib, W):
                              "frac": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                              "ms_median": round(med, 4), "ms_min": round(mn, 4)}
     cache.close()
-    return res
 
 
 def main():
@@ -361,6 +528,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode part (profiling aid)")
     ap.add_argument("--no-other-configs", action="store_true", help="skip the Llama, serving and edit measurements")
+    ap.add_argument("--only", choices=OTHER, help="run one of the other configurations alone (profiling aid)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device 5 times (calibrates rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -382,6 +550,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_per_copy": 256 << 20, "copies": 5}), flush=True)
+        return
+    if args.only:
+        print(json.dumps({args.only: other_configs(lib, W, only=args.only)}), flush=True)
         return
     print("bench: generating inputs", file=sys.stderr, flush=True)
     inp = W.grok()
@@ -487,8 +658,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic("prefill_bf16_kernel<128, false>", src_prefill),
-                     "kernel": "prefill_bf16_kernel<128, false>"},
+                     "kernel": "prefill_bf16_kernel<128, false>",
+                     "timing": "HIP events on the launch stream around the attention launch, mean of the timed steps"},
     }
+    prof_us = _profiled_us("prefill_bf16_kernel<128, false>", src_prefill)
+    if prof_us:
+        out["roofline"]["profile_avg_us"] = prof_us
+        out["roofline"]["profile_frac"] = round(flops / (prof_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)
     if not args.prefill_only:
         span_ms = mean([e[3].elapsed_time(e[4]) for e in events])
         kv_bytes = 2.0 * LAYERS * HKV * N * D * 2
@@ -503,13 +679,19 @@ def main():
                                   "traffic": _traffic("decode_bf16_kernel<128, false, false>", src_dec),
                                   "kernel": "one layer of the replayed decode graph: decode_bf16_kernel<128, false, false> "
                                             "(append, split-T attention and split combine), 32 MiB of K/V",
-                                  "layer_us": round(per_layer_ms * 1e3, 2)}
+                                  "layer_us": round(per_layer_ms * 1e3, 2),
+                                  "timing": "HIP events around the 64-layer graph replay / 64 (launch gaps included)"}
+        dec_us = _profiled_us("decode_bf16_kernel<128, false, false>", src_dec)
+        if dec_us:
+            out["roofline_decode"]["profile_avg_us"] = dec_us
+            out["roofline_decode"]["profile_frac"] = round(kv_bytes / LAYERS / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        lib.gqa_workspace_status(dec.handle, ws)
     if not args.no_other_configs and not args.prefill_only:
         print("bench: other configurations", file=sys.stderr, flush=True)
         out["other_configs"] = other_configs(lib, W)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, W)
     print(json.dumps(out), flush=True)
 
 
