@@ -252,8 +252,8 @@ def _median_ms(fn, before=None, iters=20, warm=3, reps=5):
     return ts[len(ts) // 2], ts[0]
 
 
-OTHER = ["llama_prefill", "serving_decode", "verify_chunks", "shared_prompt_decode", "holey_mask_prefill",
-         "window_prefill", "window_decode", "edit_reprefill"]
+OTHER = ["llama_prefill", "llama_decode", "serving_decode", "verify_chunks", "shared_prompt_decode",
+         "holey_mask_prefill", "window_prefill", "window_decode", "edit_reprefill", "small_latency"]
 
 
 def other_configs(lib, W, only=None):
@@ -267,6 +267,8 @@ def other_configs(lib, W, only=None):
                                              "shared_prompt_decode")
     if want("llama_prefill"):
         _llama(lib, W, res)
+    if want("llama_decode"):
+        _llama_decode(lib, W, res)
     if serving_cache:
         _serving(lib, W, res, want)
     if want("holey_mask_prefill"):
@@ -277,6 +279,8 @@ def other_configs(lib, W, only=None):
         _window_decode(lib, W, res)
     if want("edit_reprefill"):
         _edit(lib, W, res)
+    if want("small_latency"):
+        _small(lib, W, res)
     return res
 
 
@@ -297,6 +301,129 @@ def _llama(lib, W, res):
                             "frac": round(flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                             "ms_median": round(med, 4), "ms_min": round(mn, 4)}
     pre.close()
+
+
+def _llama_decode(lib, W, res):
+    """The 64 decode steps that follow the Llama-shaped prefill: each step
+    appends one token to each of the 8 sequences and decodes (gqa_decode_step,
+    one layer), reading 2 * 8 * 128 * 2 bytes per cached token.  The ~67 MB a
+    step reads fits in the 256 MB Infinity Cache, so the steps are timed twice:
+    back to back (labelled cache-resident), and with a 512 MiB device read
+    between steps, outside the timed span, which evicts the cache (a read
+    leaves no dirty lines whose write-back would compete with the step)."""
+    import torch
+    inp = W.llama()
+    sh = W.LLAMA
+    cache = lib.PagedCache(1, sh.Hkv, sh.d, sh.B * (sh.n // 16 + 8), sh.B, sh.n // 16 + 8, dtype=torch.bfloat16,
+                           rope_theta=sh.theta, max_position=sh.n + 160,
+                           free_list_order=W.page_order(sh.B * (sh.n // 16 + 8), 3003))
+    ids = list(range(sh.B))
+    O = torch.empty_like(inp.Q.cuda())
+    lib.gqa_prefill(cache.handle, 0, ids, inp.Q.cuda(), inp.K.cuda(), inp.V.cuda(), inp.mask, inp.positions, O)
+    steps = [W.decode_step_inputs(sh, 1003, t) for t in range(64)]
+    dev = [(s.q.cuda(), s.k.cuda(), s.v.cuda()) for s in steps]
+    o = torch.empty_like(dev[0][0])
+    ws = torch.zeros(lib.gqa_workspace_size(cache.handle, sh.B, sh.Hq), dtype=torch.uint8, device="cuda")
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    reset = lambda: [lib.kv_cache_truncate(cache.handle, b, sh.n) for b in ids]
+    nbytes = sum(sh.B * (sh.n + t + 1) * 2 * sh.Hkv * sh.d * 2 for t in range(64))
+    # eager pass first (uploads the rotation table), then the captures: one
+    # graph of the 64 steps and one graph per step.  A replay runs the kernels
+    # of its capture (positions 2048.. as captured), whatever the host state.
+    reset()
+    for q, k, v in dev:
+        lib.gqa_decode_step(cache.handle, 0, ids, q, k, v, o, ws)
+    torch.cuda.synchronize()
+    reset()
+    whole = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(whole):
+        for q, k, v in dev:
+            lib.gqa_decode_step(cache.handle, 0, ids, q, k, v, o, ws)
+    reset()
+    per_step = []
+    for q, k, v in dev:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lib.gqa_decode_step(cache.handle, 0, ids, q, k, v, o, ws)
+        per_step.append(g)
+    torch.cuda.synchronize()
+    out = {}
+    # cache-resident: the 64-step graph back to back (the ~67 MB a step reads
+    # stays in the 256 MB Infinity Cache from one replay to the next)
+    whole.replay()
+    spans = []
+    for _ in range(5):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        whole.replay()
+        z.record()
+        torch.cuda.synchronize()
+        spans.append(a.elapsed_time(z) * 1e3 / 64)
+    spans.sort()
+    us = spans[len(spans) // 2]
+    out["cache_resident"] = {"us_per_step": round(us, 2), "gbs": round(nbytes / 64 / (us * 1e-6) / 1e9, 1),
+                             "frac": round(nbytes / 64 / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                             "label": "LLC-resident: the steps' K/V fit in the 256 MB Infinity Cache"}
+    # flushed: a 512 MiB device read before every step, outside the timed span
+    # (it keeps the queue busy, so the events see GPU time only)
+    ev = []
+    sink = torch.zeros(64, dtype=torch.float32, device="cuda")
+    for t, g in enumerate(per_step):
+        torch.sum(flush, dim=0, keepdim=True, out=sink[t:t + 1])
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        z.record()
+        ev.append((a, z))
+    torch.cuda.synchronize()
+    us_f = [a.elapsed_time(z) * 1e3 for a, z in ev]
+    mean_f = sum(us_f) / len(us_f)
+    out["cache_flushed"] = {"us_per_step": round(mean_f, 2), "gbs": round(nbytes / 64 / (mean_f * 1e-6) / 1e9, 1),
+                            "frac": round(nbytes / 64 / (mean_f * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                            "label": "512 MiB read between steps (outside the timed span) evicts the cache"}
+    lib.gqa_workspace_status(cache.handle, ws)
+    res["llama_decode"] = {"workload": "64 gqa_decode_step calls after the Llama-shaped prefill, B=8, T=2049..2112, "
+                                       "Hq=32 Hkv=8 d=128, one layer (~67 MB of K/V per step)", **out}
+    cache.close()
+
+
+def _small(lib, W, res):
+    """Latency of the two small configurations: the float32 toy (B=1, n=4,
+    Hq=2, Hkv=1, d=4: prefill, then a decode step) and the ragged bf16 batch
+    (B=4, n=128, Hq=8, Hkv=2, d=64: prefill, then a decode step of the 4)."""
+    import torch
+    pre, steps = W.tiny()
+    tc = lib.PagedCache(1, 1, 4, 8, 1, 4, dtype=torch.float32, rope_theta=0.0)
+    Q, K, V = pre.Q.cuda(), pre.K.cuda(), pre.V.cuda()
+    O = torch.empty_like(Q)
+    q, k, v = steps[0].q.cuda(), steps[0].k.cuda(), steps[0].v.cuda()
+    o = torch.empty_like(q)
+    med_p, _ = _median_ms(lambda: lib.gqa_prefill(tc.handle, 0, [0], Q, K, V, pre.mask, pre.positions, O),
+                          before=lambda: lib.kv_cache_truncate(tc.handle, 0, 0))
+    med_d, _ = _median_ms(lambda: lib.gqa_decode_step(tc.handle, 0, [0], q, k, v, o),
+                          before=lambda: lib.kv_cache_truncate(tc.handle, 0, 4))
+    tc.close()
+    inp = W.ragged()
+    sh = inp.shape
+    rc = lib.PagedCache(1, sh.Hkv, sh.d, 64, sh.B, 16, dtype=torch.bfloat16, rope_theta=sh.theta)
+    Q, K, V = inp.Q.cuda(), inp.K.cuda(), inp.V.cuda()
+    O = torch.empty_like(Q)
+    ids = list(range(sh.B))
+    st = W.decode_step_inputs(sh, 1002, 0)
+    q, k, v = st.q.cuda(), st.k.cuda(), st.v.cuda()
+    o = torch.empty_like(q)
+    ws = torch.zeros(lib.gqa_workspace_size(rc.handle, sh.B, sh.Hq), dtype=torch.uint8, device="cuda")
+    rmed_p, _ = _median_ms(lambda: lib.gqa_prefill(rc.handle, 0, ids, Q, K, V, inp.mask, inp.positions, O),
+                           before=lambda: [lib.kv_cache_truncate(rc.handle, b, 0) for b in ids])
+    lens = [int(x) for x in inp.lengths]
+    rmed_d, _ = _median_ms(lambda: lib.gqa_decode_step(rc.handle, 0, ids, q, k, v, o, ws),
+                           before=lambda: [lib.kv_cache_truncate(rc.handle, b, lens[b]) for b in ids])
+    rc.close()
+    res["small_latency"] = {
+        "workload": "float32 toy B=1 n=4 Hq=2 Hkv=1 d=4; ragged bf16 B=4 n=128 (lengths U{1..128}) Hq=8 Hkv=2 d=64; "
+                    "per-call time of 20 back-to-back calls (median of 5 batches)",
+        "tiny_prefill_us": round(med_p * 1e3, 1), "tiny_decode_step_us": round(med_d * 1e3, 1),
+        "ragged_prefill_us": round(rmed_p * 1e3, 1), "ragged_decode_step_us": round(rmed_d * 1e3, 1)}
 
 
 def _serving(lib, W, res, want):
@@ -685,6 +812,8 @@ def main():
         if dec_us:
             out["roofline_decode"]["profile_avg_us"] = dec_us
             out["roofline_decode"]["profile_frac"] = round(kv_bytes / LAYERS / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+            out["decode"]["kernel_sum_ms"] = round(dec_us * LAYERS / 1e3, 4)
+            out["decode"]["kernel_sum_gbs"] = round(kv_bytes / (dec_us * LAYERS * 1e-6) / 1e9, 1)
         lib.gqa_workspace_status(dec.handle, ws)
     if not args.no_other_configs and not args.prefill_only:
         print("bench: other configurations", file=sys.stderr, flush=True)
