@@ -16,7 +16,8 @@ Inputs are resident in HBM before the timed region.  ``value`` is the causal
 prefill throughput 2*B*Hq*n^2*d / (append + attention time, HIP events);
 ``decode`` reports the decode KV-read rate over the 64 layers.  ``roofline``
 is the prefill attention kernel: algorithmic flops of one launch over its
-event-timed duration, against the bf16 dense MFMA peak; ``roofline_decode``
+event-timed duration, against the bf16 dense MFMA peak (beside it, as
+context, the vendor library's 8192^3 bf16 GEMM rate measured in the same run); ``roofline_decode``
 is one layer of the decode graph (one decode_bf16_kernel launch: append,
 split-T attention and split combine) against HBM.  ``cpu_baseline`` times the float64 oracle on a bounded sample of the
 same prefill (query rows spread over the sequence) on this host's cores.
@@ -86,6 +87,28 @@ def _profiled_us(kernel_key, source):
     if not rec or rec.get("source_sha256") != _sha(source):
         return None
     return rec.get("avg_us")
+
+
+def _library_gemm(torch, n=8192, reps=10):
+    """Dense bf16 GEMM rate of the vendor library (torch.matmul -> hipBLASLt)
+    on n x n x n random N(0,1) operands on this GPU: the practical matrix-core
+    rate of a plain contraction under the same clock and power limits, reported
+    beside the attention kernel's roofline as context (not its peak)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
 def _blas_info():
@@ -658,6 +681,8 @@ def main():
     ap.add_argument("--only", choices=OTHER, help="run one of the other configurations alone (profiling aid)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device 5 times (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only time the library's 8192^3 bf16 GEMM (profiling aid)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -677,6 +702,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_per_copy": 256 << 20, "copies": 5}), flush=True)
+        return
+    if args.gemm_probe:
+        print(json.dumps({"library_gemm_bf16_8192_tflops": round(_library_gemm(torch), 1)}), flush=True)
         return
     if args.only:
         print(json.dumps({args.only: other_configs(lib, W, only=args.only)}), flush=True)
@@ -792,6 +820,11 @@ def main():
     if prof_us:
         out["roofline"]["profile_avg_us"] = prof_us
         out["roofline"]["profile_frac"] = round(flops / (prof_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    gemm = _library_gemm(torch)
+    out["roofline"]["library_gemm_tflops"] = round(gemm, 1)
+    out["roofline"]["frac_of_library_gemm"] = round(attn_tflops / gemm, 4)
+    out["roofline"]["library_gemm_note"] = ("torch.matmul (hipBLASLt) bf16 8192x8192x8192 on random N(0,1) operands, "
+                                            "same GPU and run: the practical rate of a plain contraction here")
     if not args.prefill_only:
         span_ms = mean([e[3].elapsed_time(e[4]) for e in events])
         kv_bytes = 2.0 * LAYERS * HKV * N * D * 2
