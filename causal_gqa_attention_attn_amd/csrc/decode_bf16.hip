@@ -234,6 +234,14 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   bf16x8 kf[kBatch][NQ];
   u32x2 vf[kBatch][NDB];
   load_pages(phys, kf, vf);
+  // block-table entries of the next batch, requested one batch ahead so that
+  // each batch's page loads issue without a table round trip before them
+  int32_t nphys[kBatch];
+  auto load_table_ahead = [&](int p_next) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) nphys[j] = trow[tix(min(p_next + 4 * j, p_end - 1))];
+  };
+  load_table_ahead(p_first + 4 * kBatch);
 
   // rotate (pairs i, i + D/2) with rotation row csr and round to bf16: the
   // queries, and the new key with the query's rotation row
@@ -304,8 +312,9 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   for (int p0 = p_first; p0 < p_end; p0 += 4 * kBatch) {
     if (p0 != p_first) {
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) phys[j] = trow[tix(min(p0 + 4 * j, p_end - 1))];
+      for (int j = 0; j < kBatch; ++j) phys[j] = nphys[j];
       load_pages(phys, kf, vf);
+      load_table_ahead(p0 + 4 * kBatch);
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
