@@ -476,6 +476,8 @@ gqa_status launch_attention(gqa_cache* c, int32_t layer, const int32_t* seq_ids,
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cf.head_dim)));
     a.pool_bytes = static_cast<uint32_t>(c->layer_elems * c->elt);
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    a.rope_t = cf.rope_style == 1 ? c->d_rope + static_cast<int64_t>(cf.max_position) * cf.head_dim : nullptr;
+    a.rope_rows = cf.max_position;
     int rw = -1;
     for (int j = 0; j < nb; ++j) {
       const Entry& e = es[e0 + j];
@@ -512,8 +514,8 @@ GQA_EXPORT gqa_status gqa_cache_buffer_sizes(const gqa_cache_config* cfg, size_t
   if (k_pool_bytes) *k_pool_bytes = pool;
   if (v_pool_bytes) *v_pool_bytes = pool;
   if (page_table_bytes) *page_table_bytes = static_cast<size_t>(cfg->max_seqs) * cfg->max_pages_per_seq * 4;
-  if (rope_table_bytes)
-    *rope_table_bytes = cfg->rope_style == 1 ? static_cast<size_t>(cfg->max_position) * cfg->head_dim * 4 : 0;
+  if (rope_table_bytes)   // the rows, then the same values grouped by 16-byte chunk
+    *rope_table_bytes = cfg->rope_style == 1 ? 2 * static_cast<size_t>(cfg->max_position) * cfg->head_dim * 4 : 0;
   return GQA_OK;
 }
 
@@ -558,13 +560,21 @@ GQA_EXPORT gqa_status gqa_cache_create(const gqa_cache_config* cfg, void* k_pool
     const int half = cfg->head_dim / 2;
     std::vector<double> inv(half);
     for (int i = 0; i < half; ++i) inv[i] = std::pow(cfg->rope_theta, -2.0 * i / cfg->head_dim);
-    c->rope_host.resize(static_cast<size_t>(cfg->max_position) * cfg->head_dim);
-    for (int64_t p = 0; p < cfg->max_position; ++p)
+    const int64_t rows = cfg->max_position, d = cfg->head_dim;
+    c->rope_host.resize(static_cast<size_t>(2 * rows * d));
+    for (int64_t p = 0; p < rows; ++p)
       for (int i = 0; i < half; ++i) {
         const double ang = static_cast<double>(p) * inv[i];
         c->rope_host[(p * half + i) * 2] = static_cast<float>(std::cos(ang));
         c->rope_host[(p * half + i) * 2 + 1] = static_cast<float>(std::sin(ang));
       }
+    // second copy, chunk-major: 16-byte chunk j of row p at [j][p], so that
+    // consecutive positions of one chunk are adjacent in memory (the prefill
+    // kernel reads one chunk of 32 consecutive positions per instruction)
+    float* tr = c->rope_host.data() + rows * d;
+    for (int64_t j = 0; j < d / 4; ++j)
+      for (int64_t p = 0; p < rows; ++p)
+        for (int e = 0; e < 4; ++e) tr[(j * rows + p) * 4 + e] = c->rope_host[p * d + j * 4 + e];
   }
   *out = c;
   return GQA_OK;
@@ -902,6 +912,8 @@ gqa_status launch_decode_f32(gqa_cache* c, int32_t layer, int32_t B, const int32
     a.nseq = nb;
     a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(cf.head_dim)));
     a.rope = cf.rope_style == 1 ? c->d_rope : nullptr;
+    a.rope_t = cf.rope_style == 1 ? c->d_rope + static_cast<int64_t>(cf.max_position) * cf.head_dim : nullptr;
+    a.rope_rows = cf.max_position;
     for (int j = 0; j < nb; ++j) {
       a.meta.row[j] = static_cast<uint8_t>(j);
       a.meta.seq[j] = seq_ids[b0 + j];

@@ -93,7 +93,9 @@ struct AttnArgs {
   float scale;                // 1/sqrt(d)
   float scale_log2;           // log2(e)/sqrt(d)
   uint32_t pool_bytes;        // bytes of this layer's K (= V) pool; offsets into it fit 32 bits
-  const float* rope;
+  const float* rope;          // [max_position][d/2][2] or nullptr
+  const float* rope_t;        // the same values by 16-byte chunk: [d/8][max_position][4] floats
+  int32_t rope_rows;          // max_position
   AttnMeta meta;              // nseq entries
 };
 

@@ -448,12 +448,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a, int Gc
       for (int c = 0; c < NC; ++c) w[c] = *reinterpret_cast<const u32x4*>(qrow + c * 16 + half * 8);
       f32x4 cs[NC / 2][4];                   // (cos, sin) of pairs 16c + 8*half + 0..7
       if (a.rope) {
-        const float* rrow = a.rope + static_cast<int64_t>(c0 + t0 + tq) * D;
+        // chunk-major copy of the table: chunk 8c + 4*half + q4 of this lane's
+        // position; the 32 lanes of a half read 32 consecutive positions of one
+        // chunk, 512 contiguous bytes
+        const float* rcol = a.rope_t + static_cast<int64_t>(c0 + t0 + tq) * 4;
 #pragma unroll
         for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4)
-            cs[c][q4] = *reinterpret_cast<const f32x4*>(rrow + 2 * (c * 16 + half * 8) + 4 * q4);
+            cs[c][q4] = *reinterpret_cast<const f32x4*>(
+                rcol + static_cast<int64_t>(8 * c + 4 * half + q4) * a.rope_rows * 4);
       }
       float x[NC][8];
 #pragma unroll

@@ -130,7 +130,10 @@ typedef struct gqa_cache gqa_cache;
  *           inside a page, so a page of one head is V^T; logical content is the
  *           same as row-major V)
  *  page_table int32 [max_seqs][max_pages_per_seq]
- *  rope_table float32 pairs (cos, sin) [max_position][d/2]  (0 if rope_style 0) */
+ *  rope_table float32: the rotation rows, pairs (cos, sin) [max_position][d/2],
+ *           then the same values chunk-major, [d/4][max_position][4] (16-byte
+ *           chunk j of row p at [j][p]); 2 * max_position * d * 4 bytes
+ *           (0 if rope_style 0) */
 gqa_status gqa_cache_buffer_sizes(const gqa_cache_config* cfg, size_t* k_pool_bytes,
                                   size_t* v_pool_bytes, size_t* page_table_bytes,
                                   size_t* rope_table_bytes);

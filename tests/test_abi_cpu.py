@@ -64,6 +64,19 @@ def _cache(lib, **kw):
     return st, h
 
 
+def test_buffer_sizes():
+    """Pools [layers][pages][Hkv][16][d], the block table [max_seqs][max_pages_per_seq]
+    int32, and the rotation table twice (rows, then the chunk-major copy)."""
+    import causal_gqa_attention_attn_amd as lib
+    cfg = lib._cfg(num_layers=3, num_kv_heads=2, head_dim=64, page_size=16, num_pages=5, max_seqs=4,
+                   max_pages_per_seq=6, dtype=lib.BF16, rope_style=1, max_position=40, rope_theta=1e4)
+    k, v, t, r = lib.gqa_cache_buffer_sizes(cfg)
+    assert k == v == 3 * 5 * 2 * 16 * 64 * 2
+    assert t == 4 * 6 * 4
+    assert r == 2 * 40 * 64 * 4
+    cfg.rope_style = 0
+    assert lib.gqa_cache_buffer_sizes(cfg)[3] == 0
+
 def test_config_checks():
     import causal_gqa_attention_attn_amd as lib
     st, _ = _cache(lib, page_size=8)
