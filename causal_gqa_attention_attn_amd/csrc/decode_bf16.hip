@@ -22,10 +22,12 @@
 //    (token, head) columns of its group); its four waves take the split's pages in turn,
 //    each with two pages in flight; the block-table entries, the query
 //    and its rotation row are requested together before any is used;
-//  * per page: S^T[16 keys x 16 columns] = K q^T on v_mfma_f32_16x16x32_bf16 with
-//    the K rows loaded straight from the page, then O^T[d x heads] += V^T P^T
-//    on v_mfma_f32_16x16x16_bf16 with V^T read straight from the d-major page;
-//    the score accumulator is already the B operand of the second product;
+//  * per two pages of a wave (one block of 32 keys): S^T[16 keys x 16
+//    columns] = K q^T on v_mfma_f32_16x16x32_bf16 for each half of the block,
+//    K rows loaded straight from the pages in an order that makes the two
+//    score accumulators the B operand of O^T[d x heads] += V^T P^T, also on
+//    v_mfma_f32_16x16x32_bf16, whose V^T operand is 8 consecutive slots of
+//    one d-row of the d-major page: every K and V load is 16 bytes wide;
 //  * online softmax in base 2 per column; the four waves, then the splits, are
 //    combined with the log-sum-exp rule: with M = max_s m_s,
 //    O = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M);
@@ -218,21 +220,32 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
       }
     }
   }
-  auto load_pages = [&](const int64_t* ph, bf16x8 (*kf)[NQ], u32x2 (*vf)[NDB]) {
+  // A batch is the wave's two pages p0 and p0 + 4, taken as one block of 32
+  // keys.  Key order inside the block (the k index of the P.V product): k =
+  // 8*g + e is slot 8*(g%2) + e of page g/2 (g = 0..3), so that a lane's V^T
+  // operand is 8 consecutive slots of one d-row of one page, a 16-byte load.
+  // The score products take K rows in the matching order (row r of half-block
+  // v is slot 8*((r/4)%2) + 4v + r%4 of page r/8), which leaves in lane
+  // (column, g) the scores of keys k = 8g + 4v + 0..3: elements 4v..4v+3 of
+  // its B operand of the P.V product, as they stand.
+  static_assert(kBatch == 2, "a batch is two pages");
+  const int kslot0 = 8 * ((c16 >> 2) & 1) + (c16 & 3);   // K row slot of half-block 0 (+4 for half-block 1)
+  auto load_pages = [&](const int64_t* ph, bf16x8 (*kf)[NQ], u32x4* vf) {
+    const int64_t kph = c16 < 8 ? ph[0] : ph[1];
+    const int64_t vph = grp < 2 ? ph[0] : ph[1];
+    const uint16_t* kpage = kpool + (kph * Hkv + g) * (kPage * D);
+    const uint16_t* vpage = vpool + (vph * Hkv + g) * (D * kPage);
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const uint16_t* kpage = kpool + (ph[j] * Hkv + g) * (kPage * D);
-      const uint16_t* vpage = vpool + (ph[j] * Hkv + g) * (D * kPage);
+    for (int v = 0; v < 2; ++v)
 #pragma unroll
       for (int c = 0; c < NQ; ++c)
-        kf[j][c] = *reinterpret_cast<const bf16x8*>(kpage + c16 * D + c * 32 + grp * 8);
+        kf[v][c] = *reinterpret_cast<const bf16x8*>(kpage + (kslot0 + 4 * v) * D + c * 32 + grp * 8);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        vf[j][db] = *reinterpret_cast<const u32x2*>(vpage + (db * 16 + c16) * kPage + grp * 4);
-    }
+    for (int db = 0; db < NDB; ++db)
+      vf[db] = *reinterpret_cast<const u32x4*>(vpage + (db * 16 + c16) * kPage + (grp & 1) * 8);
   };
-  bf16x8 kf[kBatch][NQ];
-  u32x2 vf[kBatch][NDB];
+  bf16x8 kf[2][NQ];
+  u32x4 vf[NDB];
   load_pages(phys, kf, vf);
   // block-table entries of the next batch, requested one batch ahead so that
   // each batch's page loads issue without a table round trip before them
@@ -307,8 +320,8 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
     l_run[ch] = 0.f;
   }
 
-  // wave w takes pages p_begin + w, + 4, ...; kBatch of them are in flight at
-  // a time (pages past the split's end reload its last page and are skipped)
+  // wave w takes pages p_begin + w, + 4, ...: a batch is p0 and p0 + 4 (a
+  // second page past the split's end reloads its last page and is masked)
   for (int p0 = p_first; p0 < p_end; p0 += 4 * kBatch) {
     if (p0 != p_first) {
 #pragma unroll
@@ -316,74 +329,97 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
       load_pages(phys, kf, vf);
       load_table_ahead(p0 + 4 * kBatch);
     }
+    const bool second = p0 + 4 < p_end;
+    if (owns_new && (p_new == p0 || (second && p_new == p0 + 4))) {
+      // slot T-1 from registers: whatever the page held there is ignored
+      const int jn = p_new == p0 ? 0 : 1;
+      if (c16 == 8 * jn + 4 * (r_new >> 3) + (r_new & 3)) {
+        const int vn = (r_new >> 2) & 1;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int p = p0 + 4 * j;
-      if (p >= p_end) break;
-      if (owns_new && p == p_new) {
-        // slot T-1 from registers: whatever the page held there is ignored
-        if (c16 == r_new) {
+        for (int v = 0; v < 2; ++v)
 #pragma unroll
-          for (int c = 0; c < NQ; ++c) kf[j][c] = knew[c];
-        }
-        if (grp == (r_new >> 2)) {
-          const int e = r_new & 3;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const uint32_t word = vf[j][db][e >> 1];
-            vf[j][db][e >> 1] = (e & 1) ? ((word & 0x0000ffffu) | (vw[db] << 16)) : ((word & 0xffff0000u) | vw[db]);
-          }
-        }
+          for (int c = 0; c < NQ; ++c)
+            if (v == vn) kf[v][c] = knew[c];
       }
-      const int key0 = p * kPage + grp * 4;   // keys of this lane's rows: key0 + i
-      if (p * kPage + kPage > T) {
-        // stale slots past the length: zero their values so 0 * NaN never occurs
-        const uint32_t k01 = (key0 < T ? 0x0000ffffu : 0u) | (key0 + 1 < T ? 0xffff0000u : 0u);
-        const uint32_t k23 = (key0 + 2 < T ? 0x0000ffffu : 0u) | (key0 + 3 < T ? 0xffff0000u : 0u);
+      if (grp == 2 * jn + (r_new >> 3)) {
+        const int e = r_new & 7;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          vf[j][db][0] &= k01;
-          vf[j][db][1] &= k23;
-        }
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            if (w == (e >> 1)) {
+              const uint32_t word = vf[db][w];
+              vf[db][w] = (e & 1) ? ((word & 0x0000ffffu) | (vw[db] << 16)) : ((word & 0xffff0000u) | vw[db]);
+            }
       }
+    }
+    // this lane's V^T slots: page p0 + 4*(grp/2), slots kv0 .. kv0 + 7; those
+    // at or past the length, and all of a masked second page, are zeroed so
+    // that 0 * NaN never occurs
+    const bool dead = (grp >> 1) == 1 && !second;
+    const int kv0 = (p0 + 4 * (grp >> 1)) * kPage + 8 * (grp & 1);
+    if (dead || kv0 + 8 > T) {
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        if (ch > 0 && !two) break;
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t keep = (!dead && kv0 + 2 * w < T ? 0x0000ffffu : 0u) |
+                              (!dead && kv0 + 2 * w + 1 < T ? 0xffff0000u : 0u);
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][c], qf[ch][c], s, 0, 0, 0);
-        if (p * kPage + kPage > start + 1) {
-          // the page holds keys past the first query's position: causal mask
-          // per column (covers the keys at or past T, since every qpos < T)
+        for (int db = 0; db < NDB; ++db) vf[db][w] &= keep;
+      }
+    }
+    const int p_last = second ? p0 + 4 : p0;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      if (ch > 0 && !two) break;
+      // scores of keys kv0 + 4v + i (element i of half-block v) for this lane's column
+      f32x4 s[2];
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        s[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) s[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[v][c], qf[ch][c], s[v], 0, 0, 0);
+      }
+      if (dead) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) s[v] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+      if (p_last * kPage + kPage > start + 1) {
+        // the block holds keys past the first query's position: causal mask
+        // per column (covers the keys at or past T, since every qpos < T)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (key0 + i > qpos[ch]) s[i] = -INFINITY;
-        }
-        if (WIN && p * kPage < start + cnt - a.window) {
-          // the page holds keys before the last column's window: per column
+            if (kv0 + 4 * v + i > qpos[ch]) s[v][i] = -INFINITY;
+      }
+      if (WIN && p0 * kPage < start + cnt - a.window) {
+        // the block holds keys before the last column's window: per column
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (key0 + i <= qpos[ch] - a.window) s[i] = -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[ch], mx * sl2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[ch] - m_new);
-        m_run[ch] = m_new;
-        float pr[4];
+            if (kv0 + 4 * v + i <= qpos[ch] - a.window) s[v][i] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[ch], mx * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[ch] - m_new);
+      m_run[ch] = m_new;
+      float pr[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -m_new));
-        l_run[ch] = l_run[ch] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        s16x4 pb;
+      for (int v = 0; v < 2; ++v)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(short, static_cast<__bf16>(pr[i]));
+        for (int i = 0; i < 4; ++i) pr[4 * v + i] = __builtin_amdgcn_exp2f(fmaf(s[v][i], sl2, -m_new));
+      l_run[ch] = l_run[ch] * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+      bf16x8 pb;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          o[ch][db] *= alpha;
-          o[ch][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf[j][db]), pb,
-                                                                o[ch][db], 0, 0, 0);
-        }
+      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(pr[e]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        o[ch][db] *= alpha;
+        o[ch][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[db]), pb, o[ch][db], 0, 0, 0);
       }
     }
   }
