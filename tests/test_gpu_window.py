@@ -124,6 +124,33 @@ def test_window_odd_group_large_negative_logits(win):
     pair.check_cache([0])
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 8)])
+def test_window_prefill_second_pass_on_score_overflow(Hq, Hkv):
+    """Window 100: one key (position 150) whose score dwarfs every other, seen
+    by rows 150..249 only.  Its probability against the tile reference passes
+    2^64, so the windowed kernel takes its exact-maximum pass, which must keep
+    the window's lower edge: rows 160..249 of the pointing heads return that
+    key's value, rows 250.. do not see it.  64- and 128-token query tiles."""
+    win, n, d = 100, 300, 128
+    G = Hq // Hkv
+    say(f"case: window {win}, Hq={Hq} Hkv={Hkv}, a spike key at 150 (exact-maximum pass)")
+    shape = W.AttnShape(B=1, n=n, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=0.0)
+    inp = W.prefill_inputs(shape, 905)
+    direction = torch.zeros(d)
+    direction[3] = 1.0
+    inp.K[0, 0, 150] = (40.0 * direction).to(torch.bfloat16)
+    inp.Q[0, :G, 160:] = (40.0 * direction).to(torch.bfloat16)
+    R = _ring_pages(win, n) + 1
+    pair = Pair(1, Hkv, d, R + 4, 1, R, torch.bfloat16, 0.0, max_position=1024, window=win)
+    O, ref = pair.prefill(0, [0], inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+    compare_rows(O, ref, torch.bfloat16)
+    o = O.float().cpu()
+    for h in range(G):
+        assert torch.allclose(o[0, h, 200], inp.V[0, 0, 150].float(), atol=1e-2), "row 200 must return the spike's value"
+        assert not torch.allclose(o[0, h, 260], inp.V[0, 0, 150].float(), atol=1e-1), "row 260 is past the spike's window"
+    pair.check_cache([0])
+
+
 def test_window_long_ring_many_wraps():
     """One sequence, W = 512 on a 50-page ring: 4096 prompt tokens in chunks of
     256, then 64 decode steps, the ring wrapping five times."""
