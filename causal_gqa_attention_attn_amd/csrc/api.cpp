@@ -815,6 +815,29 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
   }
   const int pps = decode_pages_per_split(Tr.data(), B, ys);
   const WsView wv = ws_view(workspace, ws_bytes, cf.head_dim, count_d);
+  // A decode step that opens a page for its new token: when that is all the
+  // block table waits for (nothing else pending, one launch), the decode
+  // launch takes the page from its arguments and writes the entry itself, so
+  // the step needs no block-table patch launch before it.
+  std::vector<int32_t> new_page(B, -1);
+  if (k_new && B <= gqa::kMaxSeqPerLaunch && c->copies.empty() && !c->pending.empty()) {
+    bool all = true;
+    for (const auto& pe : c->pending) {
+      int hit = -1;
+      for (int b = 0; b < B && hit < 0; ++b) {
+        const int32_t pn = (T[b] - 1) / kPage;
+        const int32_t e = cf.window ? pn % cf.max_pages_per_seq : pn;
+        if (pe.first == seq_ids[b] * cf.max_pages_per_seq + e) hit = b;
+      }
+      if (hit < 0) {
+        all = false;
+        break;
+      }
+      new_page[hit] = pe.second;
+    }
+    if (all) c->pending.clear();
+    else std::fill(new_page.begin(), new_page.end(), -1);
+  }
   gqa_status st = sync_metadata(c, s);
   if (st != GQA_OK) return st;
   int64_t split_base = 0;
@@ -867,6 +890,7 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
       a.meta.zlo[j] = 0;
       a.meta.zhi[j] = n_rect;
       a.split_off[j] = off;
+      a.new_page[j] = new_page[b];
       off += static_cast<int>(split_count(Tr[b], pps));
     }
     a.split_off[nb] = off;

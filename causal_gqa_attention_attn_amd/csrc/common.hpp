@@ -110,7 +110,7 @@ struct DecodeArgs {
   int64_t vn_s0, vn_s1;
   void* k_pool;               // this layer's pool base (written only for the new token)
   void* v_pool;
-  const int32_t* table;
+  int32_t* table;             // read; written only for new_page entries
   int32_t table_w;
   int32_t window;             // sliding window (0: none); a windowed cache is a ring of table_w pages
   int32_t Hq, Hkv, d, nseq;
@@ -127,6 +127,10 @@ struct DecodeArgs {
   int32_t wait_value;         // flag value the mergers wait for (epoch, unless a test forces a give-up)
   int32_t spin_limit;         // polls of one ready flag before a merger gives up
   int32_t split_off[kMaxSeqPerLaunch + 1];
+  // physical page of the new token's slot when this call opens that page (-1
+  // otherwise): the launch takes it from here and writes its block-table
+  // entry, instead of a separate block-table patch launch before it
+  int32_t new_page[kMaxSeqPerLaunch];
   SeqMeta meta;               // start: position of the first query token; count: query tokens;
                               // row0: their first rectangular row; total: keys read (start + count)
 };

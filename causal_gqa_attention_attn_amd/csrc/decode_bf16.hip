@@ -173,6 +173,12 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   const bool owns_new = !CHUNK && a.k_new != nullptr && split == nsplit - 1;
   const int p_new = (T - 1) >> 4;
   const int r_new = (T - 1) & 15;
+  // a page this call opens for the new token: its block-table entry is not on
+  // the device yet; this launch reads the page from its arguments and writes
+  // the entry for later calls (no other split reads that page)
+  const int new_phys = owns_new ? a.new_page[b] : -1;
+  if (new_phys >= 0 && g == 0 && hgr == 0 && threadIdx.x == 0) a.table[static_cast<int64_t>(seq) * a.table_w + tix(p_new)] = new_phys;
+  auto table_at = [&](int p) -> int64_t { return new_phys >= 0 && p == p_new ? new_phys : trow[tix(p)]; };
 
   // Everything the first batch needs is requested before anything is used:
   // the block-table entries of this wave's pages, the queries, their rotation
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   const int p_first = p_begin + wave;
   int64_t phys[kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) phys[j] = trow[tix(min(p_first + 4 * j, p_end - 1))];
+  for (int j = 0; j < kBatch; ++j) phys[j] = table_at(min(p_first + 4 * j, p_end - 1));
   u32x4 qw[NCH][NQ];
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   int32_t nphys[kBatch];
   auto load_table_ahead = [&](int p_next) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) nphys[j] = trow[tix(min(p_next + 4 * j, p_end - 1))];
+    for (int j = 0; j < kBatch; ++j) nphys[j] = table_at(min(p_next + 4 * j, p_end - 1));
   };
   load_table_ahead(p_first + 4 * kBatch);
 
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
     // write the new token to the cache: the wave whose page it is, key row by
     // the lanes of row r_new, value column by the lanes of its 4-slot group
     if (p_new >= p_begin && ((p_new - p_begin) & 3) == wave) {
-      const int64_t ph = trow[tix(p_new)];
+      const int64_t ph = table_at(p_new);
       if (c16 == r_new) {
         uint16_t* kdst = kpool + ((ph * Hkv + g) * kPage + r_new) * D;
 #pragma unroll

@@ -152,3 +152,35 @@ def test_full_block_table_and_exhausted_pool():
     assert e.value.name == "OUT_OF_PAGES"
     assert lib.gqa_cache_length(pair.gpu.handle, 1, 0) == 64
     pair.check_cache([0, 1])
+
+
+def test_decode_steps_write_the_pages_they_open():
+    """Decode steps that open a page for their token write its block-table entry
+    in the decode launch itself.  Three sequences at 14, 15 and 16 tokens take
+    20 fused steps (each crosses a page boundary at a different step, one of
+    them at once), with a free order that scatters the pages; every step
+    against the oracle, then the device block tables bit for bit, then a plain
+    decode and a truncate + re-append that read those entries back."""
+    say("case: fused decode steps opening pages (block-table entries written in the launch)")
+    d, Hq, Hkv = 128, 8, 2
+    pair = Pair(1, Hkv, d, 24, 3, 8, torch.bfloat16, 1e4, max_position=1024, free_order=W.page_order(24, 73))
+    lengths = [14, 15, 16]
+    shape = W.AttnShape(B=3, n=16, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4)
+    inp = W.prefill_inputs(shape, 74, lengths=lengths)
+    O, ref = pair.prefill(0, [0, 1, 2], inp.Q, inp.K, inp.V, inp.mask, inp.positions)
+    dshape = W.AttnShape(B=3, n=1, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4)
+    for t in range(20):
+        o, r = pair.step_fused(0, [0, 1, 2], W.decode_step_inputs(dshape, 75, t))
+        compare_rows(o, r, torch.bfloat16)
+    pair.check_cache([0, 1, 2])
+    # a decode without append reads every page through the device table
+    st = W.decode_step_inputs(dshape, 76, 0)
+    lens = [pair.ref.cache_length(s, 0) for s in (0, 1, 2)]
+    o, r = pair.decode(0, [0, 1, 2], st.q, lens)
+    compare_rows(o, r, torch.bfloat16)
+    # free a page again and let the next step open it once more
+    pair.truncate(1, 32)
+    o, r = pair.step_fused(0, [1], W.decode_step_inputs(W.AttnShape(B=1, n=1, Hq=Hq, Hkv=Hkv, d=d,
+                                                                   dtype=torch.bfloat16, theta=1e4), 77, 0))
+    compare_rows(o, r, torch.bfloat16)
+    pair.check_cache([0, 1, 2])
