@@ -67,7 +67,9 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 // its instructions carry no per-column position arithmetic.  In chunk mode a
 // workgroup takes two 16-column chunks of its kv head, which share every K/V
 // load.
-template <int D, bool CHUNK, bool WIN>
+// NEWP: some sequence's new token opens a page in this launch (a.new_page);
+// launches without one take the variant that never looks at new_page.
+template <int D, bool CHUNK, bool WIN, bool NEWP>
 __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NQ = D / 32;      // k-steps of the score product
   constexpr int NDB = D / 16;     // 16-row blocks of the output
@@ -176,9 +178,12 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   // a page this call opens for the new token: its block-table entry is not on
   // the device yet; this launch reads the page from its arguments and writes
   // the entry for later calls (no other split reads that page)
-  const int new_phys = owns_new ? a.new_page[b] : -1;
+  const int new_phys = NEWP && owns_new ? a.new_page[b] : -1;
   if (new_phys >= 0 && g == 0 && hgr == 0 && threadIdx.x == 0) a.table[static_cast<int64_t>(seq) * a.table_w + tix(p_new)] = new_phys;
-  auto table_at = [&](int p) -> int64_t { return new_phys >= 0 && p == p_new ? new_phys : trow[tix(p)]; };
+  auto table_at = [&](int p) -> int64_t {
+    const int64_t t = trow[tix(p)];                 // loaded either way: no branch around the load
+    return new_phys >= 0 && p == p_new ? static_cast<int64_t>(new_phys) : t;
+  };
 
   // Everything the first batch needs is requested before anything is used:
   // the block-table entries of this wave's pages, the queries, their rotation
@@ -614,9 +619,15 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int total_splits, hipStream_t
   // chunk mode: two column chunks per workgroup
   const dim3 grid = chunk ? dim3(total_splits * ((hchunks + 1) / 2) * a.Hkv) : dim3(total_splits, a.Hkv * hchunks);
   const bool win = a.window != 0;
+  bool newp = false;
+  for (int j = 0; j < a.nseq && !chunk; ++j) newp = newp || a.new_page[j] >= 0;
   auto pick = [&](auto dv, auto cv, auto wv) {
-    hipLaunchKernelGGL((decode_bf16_kernel<decltype(dv)::value, decltype(cv)::value, decltype(wv)::value>), grid,
-                       dim3(256), 0, s, a);
+    if (newp)
+      hipLaunchKernelGGL((decode_bf16_kernel<decltype(dv)::value, decltype(cv)::value, decltype(wv)::value, true>),
+                         grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_bf16_kernel<decltype(dv)::value, decltype(cv)::value, decltype(wv)::value, false>),
+                         grid, dim3(256), 0, s, a);
   };
   using D128 = std::integral_constant<int, 128>;
   using D64 = std::integral_constant<int, 64>;
