@@ -836,12 +836,12 @@ def main():
         src_dec = os.path.join(ROOT, "causal_gqa_attention_attn_amd", "csrc", "decode_bf16.hip")
         out["roofline_decode"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                                   "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                                  "traffic": _traffic("decode_bf16_kernel<128, false, false>", src_dec),
-                                  "kernel": "one layer of the replayed decode graph: decode_bf16_kernel<128, false, false> "
+                                  "traffic": _traffic("decode_bf16_kernel<128, false, false, *>", src_dec),
+                                  "kernel": "one layer of the replayed decode graph: decode_bf16_kernel<128, false, false, false> "
                                             "(append, split-T attention and split combine), 32 MiB of K/V",
                                   "layer_us": round(per_layer_ms * 1e3, 2),
                                   "timing": "HIP events around the 64-layer graph replay / 64 (launch gaps included)"}
-        dec_us = _profiled_us("decode_bf16_kernel<128, false, false>", src_dec)
+        dec_us = _profiled_us("decode_bf16_kernel<128, false, false, *>", src_dec)
         if dec_us:
             out["roofline_decode"]["profile_avg_us"] = dec_us
             out["roofline_decode"]["profile_frac"] = round(kv_bytes / LAYERS / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
