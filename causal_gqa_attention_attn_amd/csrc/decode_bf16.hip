@@ -179,8 +179,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   // the device yet; this launch reads the page from its arguments and writes
   // the entry for later calls (no other split reads that page)
   const int new_phys = NEWP && owns_new ? a.new_page[b] : -1;
-  if (new_phys >= 0 && g == 0 && hgr == 0 && threadIdx.x == 0)
-    a.table[static_cast<int64_t>(seq) * a.table_w + tix(p_new)] = new_phys;
+  if (new_phys >= 0 && g == 0 && hgr == 0 && threadIdx.x == 0) a.table[static_cast<int64_t>(seq) * a.table_w + tix(p_new)] = new_phys;
   auto table_at = [&](int p) -> int64_t {
     const int64_t t = trow[tix(p)];                 // loaded either way: no branch around the load
     return new_phys >= 0 && p == p_new ? static_cast<int64_t>(new_phys) : t;
