@@ -312,7 +312,7 @@ gqa_status hip_fail(hipError_t e, const char* what) {
 }
 
 gqa_status launch_copies(gqa_cache* c, const std::vector<std::pair<int32_t, int32_t>>& copies, hipStream_t s) {
-  for (size_t i0 = 0; i0 < copies.size(); i0 += gqa::kMaxPatchPerLaunch) {
+  for (size_t i0 = 0; i0 < copies.size(); i0 += gqa::kMaxCopiesPerLaunch) {
     gqa::CopyArgs a;
     std::memset(&a, 0, sizeof(a));
     a.k_pool = c->k_pool;
@@ -320,7 +320,7 @@ gqa_status launch_copies(gqa_cache* c, const std::vector<std::pair<int32_t, int3
     a.layer_stride = c->layer_elems;
     a.page_elems = c->page_elems;
     a.elt_bytes = c->elt;
-    a.n = static_cast<int32_t>(std::min<size_t>(copies.size() - i0, gqa::kMaxPatchPerLaunch));
+    a.n = static_cast<int32_t>(std::min<size_t>(copies.size() - i0, gqa::kMaxCopiesPerLaunch));
     for (int j = 0; j < a.n; ++j) {
       a.src[j] = copies[i0 + j].first;
       a.dst[j] = copies[i0 + j].second;
@@ -365,8 +365,10 @@ gqa_status sync_metadata(gqa_cache* c, hipStream_t s) {
     gqa::PatchArgs pa;
     pa.table = c->d_table;
     pa.n = 0;
-    for (; i < c->pending.size() && pa.n < gqa::kMaxPatchPerLaunch; ++i, ++pa.n) {
-      pa.index[pa.n] = c->pending[i].first;
+    pa.base = c->pending[i].first;        // entries are in ascending index order
+    for (; i < c->pending.size() && pa.n < gqa::kMaxPatchPerLaunch && c->pending[i].first - pa.base < 65536;
+         ++i, ++pa.n) {
+      pa.offset[pa.n] = static_cast<uint16_t>(c->pending[i].first - pa.base);
       pa.value[pa.n] = c->pending[i].second;
     }
     hipError_t e = gqa::launch_table_patch(pa, s);

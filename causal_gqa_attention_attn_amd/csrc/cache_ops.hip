@@ -17,7 +17,7 @@
 namespace gqa {
 
 __global__ __launch_bounds__(256) void table_patch_kernel(PatchArgs a) {
-  for (int i = threadIdx.x; i < a.n; i += blockDim.x) a.table[a.index[i]] = a.value[i];
+  for (int i = threadIdx.x; i < a.n; i += blockDim.x) a.table[a.base + a.offset[i]] = a.value[i];
 }
 
 hipError_t launch_table_patch(const PatchArgs& a, hipStream_t s) {

@@ -11,7 +11,9 @@ constexpr int kPage = 16;          // tokens per page
 constexpr int kMaxSeqPerLaunch = 64;
 constexpr int kMaxRunsPerLaunch = 144;   // entries of one attention launch
 constexpr int kMaxRowsPerLaunch = 64;    // batch rows of one attention launch (row index fits 8 bits)
-constexpr int kMaxPatchPerLaunch = 496;   // block-table entries (or page copies) per launch; the arguments stay under 4 KiB
+constexpr int kMaxCopiesPerLaunch = 496;  // page copies per launch; the arguments stay under 4 KiB
+constexpr int kMaxPatchPerLaunch = 672;   // block-table entries per launch (16-bit offsets from a base
+                                          // index, 32-bit pages: the arguments stay under 4 KiB)
 constexpr int kMaxSplitDecode = 128;   // splits per sequence in one decode launch
 constexpr int kDecodeMergers = 4;      // splits of a sequence that combine the split records
 constexpr int64_t kStaticScratchBytes = int64_t{48} << 20;   // the library's static split-T scratch per device
@@ -60,7 +62,8 @@ struct AttnMeta {
 struct PatchArgs {
   int32_t* table;
   int32_t n;
-  int32_t index[kMaxPatchPerLaunch];
+  int32_t base;                         // entry i goes to table[base + offset[i]]
+  uint16_t offset[kMaxPatchPerLaunch];
   int32_t value[kMaxPatchPerLaunch];
 };
 
@@ -143,8 +146,8 @@ struct CopyArgs {
   int64_t page_elems;         // elements of one page (all kv heads)
   int32_t n;
   int32_t elt_bytes;
-  int32_t src[kMaxPatchPerLaunch];
-  int32_t dst[kMaxPatchPerLaunch];
+  int32_t src[kMaxCopiesPerLaunch];
+  int32_t dst[kMaxCopiesPerLaunch];
 };
 
 // Every argument block stays within 4 KiB, the kernel-argument size every
