@@ -822,6 +822,7 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
   // launch takes the page from its arguments and writes the entry itself, so
   // the step needs no block-table patch launch before it.
   std::vector<int32_t> new_page(B, -1);
+  std::vector<std::pair<int32_t, int32_t>> fused;   // the entries the launch writes (restored if it fails)
   if (k_new && B <= gqa::kMaxSeqPerLaunch && c->copies.empty() && !c->pending.empty()) {
     bool all = true;
     for (const auto& pe : c->pending) {
@@ -837,11 +838,14 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
       }
       new_page[hit] = pe.second;
     }
-    if (all) c->pending.clear();
+    if (all) fused.swap(c->pending);
     else std::fill(new_page.begin(), new_page.end(), -1);
   }
   gqa_status st = sync_metadata(c, s);
-  if (st != GQA_OK) return st;
+  if (st != GQA_OK) {
+    c->pending.insert(c->pending.end(), fused.begin(), fused.end());
+    return st;
+  }
   int64_t split_base = 0;
   for (int b0 = 0; b0 < B; b0 += kMaxSeqPerLaunch) {
     const int nb = std::min(B - b0, kMaxSeqPerLaunch);
@@ -897,7 +901,10 @@ gqa_status launch_split(gqa_cache* c, int32_t layer, int32_t B, const int32_t* s
     }
     a.split_off[nb] = off;
     hipError_t e = gqa::launch_decode_bf16(a, off, s);
-    if (e != hipSuccess) return hip_fail(e, "split attention launch");
+    if (e != hipSuccess) {
+      c->pending.insert(c->pending.end(), fused.begin(), fused.end());
+      return hip_fail(e, "split attention launch");
+    }
     split_base += off;
   }
   return GQA_OK;

@@ -1,8 +1,9 @@
 """GPU edge cases against the float64 oracle: empty calls, rows without a valid
 token, a decode over a single cached token, positions at the end of the
-rotation table, a sequence that fills its block table exactly and a pool that
-runs out exactly.  Every rejected call must leave the cache unchanged and match
-the oracle's error class."""
+rotation table, a sequence that fills its block table exactly, a pool that
+runs out exactly, and block-table writes spread over several patch launches.
+Every rejected call must leave the cache unchanged and match the oracle's
+error class."""
 import sys
 
 import numpy as np
@@ -184,3 +185,26 @@ def test_decode_steps_write_the_pages_they_open():
                                                                    dtype=torch.bfloat16, theta=1e4), 77, 0))
     compare_rows(o, r, torch.bfloat16)
     pair.check_cache([0, 1, 2])
+
+
+def test_block_table_patches_split_by_count_and_by_index_span():
+    """One append opens 40 x 38 = 1520 block-table entries.  Twenty sequences
+    have neighbouring ids (760 entries within 40 960 table indexes: more than
+    one patch launch holds), twenty are spread over ids 24..100 (indexes more
+    than 65 535 apart: the 16-bit offsets of one launch cannot reach).  The
+    device block tables must equal the oracle's bit for bit, and a decode of
+    every sequence reads its pages through them."""
+    say("case: 1520 block-table entries in one append, split by count and by index span")
+    d, Hq, Hkv, L = 64, 4, 2, 600
+    ids = list(range(20)) + [24 + 4 * i for i in range(20)]
+    pages = len(ids) * 38 + 16
+    pair = Pair(1, Hkv, d, pages, max(ids) + 1, 2048, torch.bfloat16, 1e4, max_position=1024,
+                free_order=W.page_order(pages, 78))
+    shape = W.AttnShape(B=len(ids), n=L, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4)
+    inp = W.prefill_inputs(shape, 79)
+    pair.append(0, ids, inp.K, inp.V, inp.mask, inp.positions)
+    pair.check_cache(ids)
+    st = W.decode_step_inputs(W.AttnShape(B=len(ids), n=1, Hq=Hq, Hkv=Hkv, d=d, dtype=torch.bfloat16, theta=1e4),
+                              80, 0)
+    o, r = pair.decode(0, ids, st.q, [L] * len(ids))
+    compare_rows(o, r, torch.bfloat16)
