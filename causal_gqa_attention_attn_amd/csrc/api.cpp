@@ -761,9 +761,27 @@ int32_t next_epoch() { return static_cast<int32_t>(g_epoch.fetch_add(1) % 0x3fff
 // (kv head x column chunk) rows of the grid for ncol (token, head) columns
 int64_t split_ys(const gqa_cache* c, int64_t ncol) { return c->cfg.num_kv_heads * ceil_div(ncol, 16); }
 
+// Workgroups of the split-T kernel the device holds at once: two per compute
+// unit (its launch bounds), read once per process from the current device.
+int64_t decode_resident_workgroups() {
+  static std::atomic<int> cus{0};
+  int n = cus.load();
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus.store(n);
+  }
+  return 2 * static_cast<int64_t>(n);
+}
+
 // Pages per split: enough workgroups to fill the chip (about the target count),
 // at least kDecodeMinPages pages each, at most kMaxSplitDecode splits per
-// sequence (the in-kernel combine stages one weight per split in LDS).
+// sequence (the in-kernel combine stages one weight per split in LDS).  A grid
+// a little larger than the workgroups the device holds at once would run a
+// short second round, and each sequence's combine waits for its last split:
+// when longer splits (under twice as long) fit the grid in one round, take them.
 int decode_pages_per_split(const int32_t* T, int B, int64_t ys) {
   int64_t total_pages = 0, max_pages = 0;
   for (int b = 0; b < B; ++b) {
@@ -773,6 +791,20 @@ int decode_pages_per_split(const int32_t* T, int B, int64_t ys) {
   }
   int64_t pps = std::max<int64_t>(kDecodeMinPages, ceil_div(total_pages * ys, kDecodeTargetBlocks));
   pps = std::max<int64_t>(pps, ceil_div(max_pages, gqa::kMaxSplitDecode));
+  auto grid = [&](int64_t p) {
+    int64_t n = 0;
+    for (int b = 0; b < B; ++b) n += std::max<int64_t>(1, ceil_div(ceil_div(T[b], kPage), p));
+    return n * ys;
+  };
+  const int64_t resident = decode_resident_workgroups();
+  const int64_t n0 = grid(pps);
+  if (n0 > resident && n0 <= 2 * resident) {
+    for (int64_t p = pps + 1; p < 2 * pps; ++p)
+      if (grid(p) <= resident) {
+        pps = p;
+        break;
+      }
+  }
   return static_cast<int>(pps);
 }
 
