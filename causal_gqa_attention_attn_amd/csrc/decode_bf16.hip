@@ -102,8 +102,12 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
     gsplit = blockIdx.x;
   }
   const int hcb0 = hgr * NCH;                       // first column chunk of this workgroup
+  // this workgroup's sequence: the last b with split_off[b] <= gsplit (the
+  // offsets increase strictly), found by binary lifting over the arguments
   int b = 0;
-  while (b + 1 < a.nseq && a.split_off[b + 1] <= gsplit) ++b;
+#pragma unroll
+  for (int step = kMaxSeqPerLaunch / 2; step >= 1; step >>= 1)
+    if (b + step < a.nseq && a.split_off[b + step] <= gsplit) b += step;
   const int split = gsplit - a.split_off[b];
   const int nsplit = a.split_off[b + 1] - a.split_off[b];
   const int seq = a.meta.seq[b];
